@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of one device's share of a blockwise ring-attention forward.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A bench "step" is one whole ring_attn_forward: every ring step of the
+device's share (the double-buffered receive of the next K/V block on a side
+stream, the causal-tiled step kernels) and the fused finalize, over seeded
+synthetic Q/K/V already resident in HBM. Prints ONE JSON line.
+
+value     effective causal attention TFLOP/s of the whole forward:
+          sum over steps of 4 * head_dim * heads_q * batch * (visible pairs),
+          divided by the forward's wall time (HIP events around K forwards).
+roofline  for the dominant kernel (the bf16 step kernel): the same algorithmic
+          FLOPs per launch divided by its average launch duration, measured
+          with HIP events recorded around every step launch inside the timed
+          forwards, against the MI355X dense bf16 MFMA peak.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3         # MI355X fp32 vector
+DEFAULT_WORKLOAD = "zigzag128k_8dev_gqa"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def effective_flops(wl, pairs):
+    return [4.0 * wl.head_dim * wl.heads_q * wl.batch * p for p in pairs]
+
+
+def cpu_baseline(wl, rank, budget_s=12.0):
+    """Time the float64 CPU oracle on a bounded sample of the same share."""
+    import oracle
+    import ring_inputs
+    positions = oracle.device_positions(wl.partition, wl.world, rank, wl.local_len)
+    G = wl.heads_q // wl.heads_kv
+    kh = ring_inputs.head(wl, "k", 0, 0)
+    vh = ring_inputs.head(wl, "v", 0, 0)
+    k_pos = np.arange(wl.total_len)
+    rng = np.random.default_rng(0)
+    n_rows = 8
+    spent = 0.0
+    flops = 0.0
+    rows_done = 0
+    heads_done = 0
+    while spent < budget_s and n_rows <= wl.local_len:
+        rows = np.sort(rng.choice(wl.local_len, size=n_rows, replace=False))
+        pos = positions[rows]
+        qs = [ring_inputs.rows(wl, "q", 0, h, pos) for h in range(G)]
+        t0 = time.perf_counter()
+        for q in qs:
+            oracle.attention_rows(q, pos, kh, vh, k_pos, wl.causal)
+        dt = time.perf_counter() - t0
+        spent += dt
+        vis = oracle.visible_pair_count(pos, k_pos, wl.causal)
+        flops += 4.0 * wl.head_dim * vis * G
+        rows_done += n_rows
+        heads_done = G
+        n_rows *= 2
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    return {
+        "value": flops / spent / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{rows_done} query rows of device {rank} x {heads_done} query heads (one KV group), "
+                  f"float64 full softmax over all {wl.total_len} global keys, {spent:.1f} s of CPU time; "
+                  f"effective FLOPs counted as for the GPU",
+    }
+
+
+def traffic_from_profile(kernel_name, workload_name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel_name}_{workload_name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    src = os.path.join(ROOT, "ring_attention_blockwise_amd", "csrc", "step_bf16.hip")
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != digest:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--rank", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU: the ring is simulated on a single device "
+                                   "(one device's share at its real shape); run with --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+    import ring_inputs
+    import ring_attention_blockwise_amd as ra
+    from ring_attention_blockwise_amd import harness
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    ra.lib()  # fail loudly if the HIP library is not built
+
+    wl = ring_inputs.WORKLOADS[args.workload]
+    rank = wl.ranks[0] if args.rank is None else args.rank
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    share = harness.build_share(wl, rank, dev)
+    torch.cuda.synchronize()
+    log(f"built {wl.name} share of device {rank} in {time.time() - t0:.1f} s")
+
+    pairs = harness.step_pairs(wl, rank)
+    flops = effective_flops(wl, pairs)
+    total_flops = sum(flops)
+    launched = [s for s in range(wl.world) if pairs[s] > 0]
+
+    out, lse = harness.alloc_outputs(share)
+    ws = harness.alloc_workspace(share)
+    copy_stream = torch.cuda.Stream()
+    cur = torch.cuda.current_stream()
+    K, Wm = args.steps, args.warmup
+    events = [ra.StepEvents(2 * wl.world) for _ in range(K)]
+
+    for _ in range(Wm):
+        harness.run_forward(share, copy_stream=copy_stream, workspace=ws, out=out, lse=lse)
+    torch.cuda.synchronize()
+    log(f"warmup done ({Wm} forwards)")
+
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(cur)
+    wall0 = time.perf_counter()
+    for i in range(K):
+        harness.run_forward(share, copy_stream=copy_stream, workspace=ws, out=out, lse=lse,
+                            step_events=events[i])
+    stop.record(cur)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / K
+    log(f"timed {K} forwards: {ms_per_step:.3f} ms each (host wall {1e3 * wall / K:.3f} ms)")
+
+    kernel_ms = 0.0
+    per_step_ms = np.zeros(wl.world)
+    for ev in events:
+        for s in launched:
+            t = ev.elapsed_ms(2 * s, 2 * s + 1)
+            per_step_ms[s] += t / K
+            kernel_ms += t
+    n_launch = K * len(launched)
+    avg_launch_ms = kernel_ms / max(1, n_launch)
+    flops_per_launch = sum(flops[s] for s in launched) / max(1, len(launched))
+    achieved = flops_per_launch / (avg_launch_ms * 1e-3) / 1e12 if n_launch else 0.0
+    bf16 = wl.dtype == "bf16"
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
+    kernel_name = "step_bf16" if bf16 else "step_f32"
+    traffic = traffic_from_profile(kernel_name, wl.name)
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(wl, rank)
+
+    rec = {
+        "metric": "effective causal attention TFLOP/s per ring step at 1 GPU; % of bf16 MFMA peak",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic (seeded N(0,1) Q/K/V, bf16-rounded)",
+        "config": {
+            "workload": wl.name, "description": wl.description, "batch": wl.batch, "heads_q": wl.heads_q,
+            "heads_kv": wl.heads_kv, "head_dim": wl.head_dim, "local_len": wl.local_len,
+            "global_seq_len": wl.total_len, "world": wl.world, "rank": rank, "partition": wl.partition,
+            "ring_steps": wl.world, "parallelism": "one device's share of a simulated ring",
+        },
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "effective_tflop_per_forward": round(total_flops / 1e12, 4),
+        "step_kernel": {
+            "launches_per_forward": len(launched),
+            "avg_launch_ms": round(avg_launch_ms, 4),
+            "per_step_ms": [round(x, 4) for x in per_step_ms.tolist()],
+            "tflops": round(achieved, 2),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    for ev in events:
+        ev.close()
+
+
+if __name__ == "__main__":
+    main()

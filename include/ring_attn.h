@@ -1,0 +1,211 @@
+/*
+ * ring_attn.h — C ABI of the per-device blockwise ring-attention step for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One device keeps a local query block Q_i and folds key/value blocks K_j, V_j
+ * into a running online-softmax state (O, m, l), one ring step at a time; a
+ * finalize pass turns the state into the attention output and its log-sum-exp.
+ *
+ * Sources (pages and sections):
+ *   [HC]  "distributed training hands-on code" (LLM-101-CN), section 6.2
+ *         (block_attention, ring_send_recv_kv, forward): S = Q K^T / sqrt(d),
+ *         running max M, running sum L, unnormalised O; forward ends with O / L.
+ *   [RS]  "Ring Attention and Sequence Parallelism" (airsota M4-051), sections 3
+ *         and 4: K/V blocks travel around a ring of n devices while the local
+ *         block computes (double buffering); causal blocks above the diagonal
+ *         are skipped; zigzag gives device i its segment and its mirror.
+ *   [L30] Lecture 30 "TP/PP/SP/CP", section 3.2 (ring walk-through, causal
+ *         imbalance, zigzag/striped) and 3.4 (the ring carries the few GQA KV
+ *         heads).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout.    Every tensor is dense, row-major [batch, heads, rows, head_dim]
+ *            ([HC] forward: bs, heads, q_len, d), 16-byte aligned. Row vectors
+ *            m, l, lse are [batch, heads_q, q_len].
+ * Memory.    Tensor arguments are DEVICE pointers; descriptors, segment and
+ *            pointer arrays are HOST memory. The caller allocates and owns every
+ *            buffer, including the workspace. The library allocates no device
+ *            memory.
+ * Streams.   `stream` arguments are hipStream_t handles passed as void*
+ *            (NULL = the default stream). Calls only enqueue work and return;
+ *            nothing synchronises the device.
+ * Errors.    Every entry point returns an ra_status. All arguments are checked
+ *            on the host before any work is enqueued, so on any error nothing
+ *            is written. A failed HIP call returns RA_ERR_HIP.
+ *            ring_attn_last_error() gives a message for the calling thread.
+ * GQA.       Query head h reads KV head h / (heads_q / heads_kv) — contiguous
+ *            groups ([L30] 3.4, 8.3: 8 Q heads per KV head per GPU).
+ * Causality. A key is visible to a query iff pos_k <= pos_q (lower triangle,
+ *            diagonal included; [L30] 3.2). Positions come from segments.
+ * State.     (O, m, l) is kept in base 2: with t_j = log2(e) * scale * q.k_j,
+ *            O = sum_j 2^(t_j - m) v_j and l = sum_j 2^(t_j - m) over the keys
+ *            folded so far. m is a reference exponent no smaller than
+ *            max_j t_j - 8 (it is raised lazily, which is exact: any reference
+ *            gives the same O / l). The empty state is m = -inf, l = 0, O = 0.
+ *            This is [HC]'s (M, L, O) with M expressed in base 2.
+ */
+#ifndef RING_ATTN_H
+#define RING_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+#define RA_OK               0
+#define RA_ERR_INVALID_ARG (-1)   /* bad size, pointer, segment or flag        */
+#define RA_ERR_UNSUPPORTED (-2)   /* valid but not built: head_dim or dtype    */
+#define RA_ERR_WORKSPACE   (-3)   /* workspace pointer NULL or too small        */
+#define RA_ERR_HIP         (-4)   /* a HIP runtime call failed                  */
+
+/* ---- element types ------------------------------------------------------ */
+#define RA_F32  0                 /* float32 Q/K/V/out; fp32 arithmetic         */
+#define RA_BF16 1                 /* bfloat16 Q/K/V/out; fp32 accumulation      */
+
+/* ---- partitions of the global sequence over `world` devices --------------- */
+#define RA_PART_CONTIGUOUS 0      /* device r: tokens [r*c, (r+1)*c)            */
+#define RA_PART_ZIGZAG     1      /* device r: chunks r and 2w-1-r of c/2 ([RS] 4) */
+#define RA_PART_STRIPED    2      /* device r: tokens r, r+w, r+2w, ... ([L30] 3.2) */
+
+/* ---- ring_attn_step flags ------------------------------------------------ */
+#define RA_STEP_INIT 1            /* ignore the incoming state: start empty     */
+
+/* Global positions of a run of local rows: row i of the run has position
+ * start + i * stride. */
+typedef struct {
+  int64_t start;
+  int64_t len;
+  int64_t stride;                 /* >= 1 */
+} ra_segment;
+
+/* One ring step: a local query block against one key/value block.
+ * Local row r of Q lies in q_seg[0] if r < q_seg[0].len, else in q_seg[1];
+ * likewise for K/V rows. The lens of a side's segments add up to its row count.
+ * n_q_seg / n_kv_seg are 1 or 2 (0 is allowed only when causal == 0). */
+typedef struct {
+  int32_t batch;
+  int32_t heads_q;
+  int32_t heads_kv;               /* heads_q % heads_kv == 0 */
+  int32_t head_dim;               /* 64 or 128 */
+  int64_t q_len;                  /* local query rows (may be 0) */
+  int64_t kv_len;                 /* rows of this K/V block (may be 0) */
+  int32_t dtype;                  /* RA_F32 or RA_BF16 */
+  int32_t causal;                 /* 0 or 1 */
+  float   scale;                  /* softmax scale; <= 0 means 1/sqrt(head_dim) */
+  int32_t n_q_seg;
+  int32_t n_kv_seg;
+  ra_segment q_seg[2];
+  ra_segment kv_seg[2];
+} ra_step_desc;
+
+/* Fold one K/V block into the running state ([HC] 6.2 block_attention;
+ * causal tile skipping per [RS] 4/6 and [L30] 3.2).
+ *   q      [B, Hq,  q_len,  d]  dtype        read
+ *   k, v   [B, Hkv, kv_len, d]  dtype        read
+ *   o_acc  [B, Hq,  q_len,  d]  fp32         read (unless RA_STEP_INIT), written
+ *   m, l   [B, Hq,  q_len]      fp32         read (unless RA_STEP_INIT), written
+ *   flags  0 or RA_STEP_INIT.
+ * Rows that see no key of this block are left untouched — or, with
+ * RA_STEP_INIT, set to the empty state. */
+int ring_attn_step(const ra_step_desc* desc, const void* q, const void* k, const void* v,
+                   float* o_acc, float* m, float* l, int32_t flags, void* stream);
+
+/* Combine two states over the same rows: (a) <- (a) (+) (b). The fold of [HC]
+ * 6.2 written for two partial states; commutative and associative. Uses
+ * batch, heads_q, q_len and head_dim of desc. */
+int ring_attn_merge(const ra_step_desc* desc, float* o_a, float* m_a, float* l_a,
+                    const float* o_b, const float* m_b, const float* l_b, void* stream);
+
+/* Normalise a state ([HC] 6.2: O / L) and write LSE = ln(2) * (m + log2 l)
+ * (natural log). A row with l == 0 gets out = 0 and lse = -inf.
+ *   out [B, Hq, q_len, d] in desc->dtype; lse [B, Hq, q_len] fp32 (may be NULL). */
+int ring_attn_finalize(const ra_step_desc* desc, const float* o_acc, const float* m,
+                       const float* l, void* out, float* lse, void* stream);
+
+/* One device's share of a simulated ring ([RS] 3-4, [HC] 6.2 forward). */
+typedef struct {
+  int32_t batch;
+  int32_t heads_q;
+  int32_t heads_kv;
+  int32_t head_dim;
+  int64_t local_len;              /* c: rows per device, also rows per K/V block */
+  int32_t dtype;
+  int32_t causal;
+  float   scale;                  /* <= 0 means 1/sqrt(head_dim) */
+  int32_t world;                  /* n >= 1 simulated devices */
+  int32_t rank;                   /* this device, 0 <= rank < world */
+  int32_t partition;              /* RA_PART_* */
+  int32_t reverse_order;          /* 0: step s uses block (rank - s) mod n (blocks
+                                     are sent to rank + 1, as [HC]'s code does);
+                                     1: block (rank + s) mod n ([HC]'s 6.1 text) */
+} ra_ring_desc;
+
+/* Bytes of workspace ring_attn_forward needs: two receive slots for one K/V
+ * block each, the fp32 state and alignment padding. Returns 0 on a bad desc. */
+size_t ring_attn_forward_workspace_size(const ra_ring_desc* desc);
+
+/* Run the whole ring for one device: n steps, then finalize.
+ *   q_local        [B, Hq, c, d] dtype, rows in this device's partition order.
+ *   k_blocks[j],
+ *   v_blocks[j]    HOST arrays of `world` DEVICE pointers: the K/V block device j
+ *                  holds, [B, Hkv, c, d], rows in device j's partition order.
+ *                  Block rank is used in place; every other block is first
+ *                  copied into a receive slot of the workspace by
+ *                  hipMemcpyAsync on copy_stream while the previous step
+ *                  computes on compute_stream (the simulated receive; events
+ *                  order the two streams, two slots alternate).
+ *   out, lse       as ring_attn_finalize.
+ *   compute_stream, copy_stream  hipStream_t (distinct; copy_stream may be NULL
+ *                  to copy on compute_stream, which serialises the receive).
+ *   step_events    NULL, or a HOST array of 2*world hipEvent_t handles; the
+ *                  driver records events[2s] / events[2s+1] on compute_stream
+ *                  right before / after step s's kernel (both at the same point
+ *                  when step s has no visible key and launches nothing).
+ * Steps whose block has no key visible to any local row launch no kernel;
+ * the block is still received. Step kernels never read a slot while it is
+ * being filled. */
+int ring_attn_forward(const ra_ring_desc* desc, const void* q_local,
+                      const void* const* k_blocks, const void* const* v_blocks,
+                      void* out, float* lse, void* workspace, size_t workspace_bytes,
+                      void* compute_stream, void* copy_stream, void* const* step_events);
+
+/* ---- host-only helpers (no device work) ---------------------------------- */
+
+/* Segments of device `rank`'s local rows under `partition` (RA_PART_*).
+ * Writes up to 2 segments to segs and their count to n_segs. */
+int ring_attn_partition_segments(int32_t partition, int32_t world, int32_t rank,
+                                 int64_t local_len, ra_segment* segs, int32_t* n_segs);
+
+/* Fill a step descriptor for ring step `step` of desc: the local rows of
+ * desc->rank against the block of device block_owner(step). Writes the block
+ * owner to *owner (may be NULL). */
+int ring_attn_ring_step_desc(const ra_ring_desc* desc, int32_t step, ra_step_desc* out,
+                             int32_t* owner);
+
+/* Number of visible (query, key) pairs of one (batch, query head) of a step:
+ * q_len * kv_len when not causal. Returns -1 on an invalid descriptor. */
+int64_t ring_attn_visible_pairs(const ra_step_desc* desc);
+
+/* Message of the last error on the calling thread ("" if none). */
+const char* ring_attn_last_error(void);
+
+/* ABI version of this header (major * 100 + minor). */
+int32_t ring_attn_abi_version(void);
+
+/* Timing helpers for callers without their own HIP bindings: create n
+ * timing-enabled hipEvent_t into events[n]; elapsed ms between two recorded
+ * events (after they completed); destroy. */
+int ring_attn_events_create(int32_t n, void** events);
+int ring_attn_event_elapsed_ms(void* start, void* stop, float* ms);
+int ring_attn_events_destroy(int32_t n, void* const* events);
+int ring_attn_synchronize(void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RING_ATTN_H */

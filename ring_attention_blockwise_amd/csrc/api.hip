@@ -1,0 +1,534 @@
+// C ABI of libring_attn: argument checks, kernel dispatch and the ring driver.
+//
+// Every entry point validates all of its arguments on the host before it
+// enqueues anything, so an error leaves every buffer untouched.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "common.h"
+#include "ring_attn.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(RA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxRows = (int64_t)1 << 30;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t count_le(const ra_segment& s, int64_t x) {
+  if (x < s.start) return 0;
+  const int64_t c = (x - s.start) / s.stride + 1;
+  return c < s.len ? c : s.len;
+}
+
+// Shape/segment checks shared by step, merge and finalize.
+int check_shape(const ra_step_desc* d, bool need_kv) {
+  if (d == nullptr) return fail(RA_ERR_INVALID_ARG, "desc is NULL");
+  if (d->batch < 0 || d->heads_q <= 0 || d->heads_kv <= 0)
+    return fail(RA_ERR_INVALID_ARG, "batch must be >= 0 and head counts > 0");
+  if (d->heads_q % d->heads_kv != 0)
+    return fail(RA_ERR_INVALID_ARG, "heads_q (%d) must be a multiple of heads_kv (%d)", d->heads_q, d->heads_kv);
+  if (d->q_len < 0 || d->q_len > kMaxRows) return fail(RA_ERR_INVALID_ARG, "q_len out of range");
+  if (need_kv && (d->kv_len < 0 || d->kv_len > kMaxRows)) return fail(RA_ERR_INVALID_ARG, "kv_len out of range");
+  if (d->dtype != RA_F32 && d->dtype != RA_BF16) return fail(RA_ERR_UNSUPPORTED, "dtype %d not supported", d->dtype);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(RA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
+  if (!std::isfinite(d->scale)) return fail(RA_ERR_INVALID_ARG, "scale is not finite");
+  return RA_OK;
+}
+
+int check_segments(const ra_segment* segs, int32_t n, int64_t rows, int causal, const char* side) {
+  if (n < 0 || n > 2) return fail(RA_ERR_INVALID_ARG, "%s: segment count %d (0..2)", side, n);
+  if (n == 0) {
+    if (causal) return fail(RA_ERR_INVALID_ARG, "%s: causal steps need position segments", side);
+    return RA_OK;
+  }
+  int64_t total = 0;
+  for (int i = 0; i < n; ++i) {
+    if (segs[i].len < 0 || segs[i].stride < 1 || segs[i].start < 0)
+      return fail(RA_ERR_INVALID_ARG, "%s: segment %d needs len >= 0, stride >= 1, start >= 0", side, i);
+    if (segs[i].len > 0 && (segs[i].start > INT64_MAX / 4 - (segs[i].len - 1) * segs[i].stride))
+      return fail(RA_ERR_INVALID_ARG, "%s: segment %d positions overflow", side, i);
+    total += segs[i].len;
+  }
+  if (total != rows)
+    return fail(RA_ERR_INVALID_ARG, "%s: segment lengths add up to %lld, rows are %lld", side, (long long)total,
+                (long long)rows);
+  return RA_OK;
+}
+
+int check_step_desc(const ra_step_desc* d) {
+  int rc = check_shape(d, true);
+  if (rc) return rc;
+  if (d->causal != 0 && d->causal != 1) return fail(RA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  rc = check_segments(d->q_seg, d->n_q_seg, d->q_len, d->causal, "q");
+  if (rc) return rc;
+  return check_segments(d->kv_seg, d->n_kv_seg, d->kv_len, d->causal, "kv");
+}
+
+ra::StepArgs make_args(const ra_step_desc* d) {
+  ra::StepArgs a{};
+  a.q_len = d->q_len;
+  a.kv_len = d->kv_len;
+  a.batch = d->batch;
+  a.heads_q = d->heads_q;
+  a.heads_kv = d->heads_kv;
+  a.group = d->heads_q / d->heads_kv;
+  const double scale = d->scale > 0.0f ? (double)d->scale : 1.0 / std::sqrt((double)d->head_dim);
+  a.scale_log2 = (float)(scale * 1.4426950408889634074);
+  a.causal = d->causal;
+  a.n_q_seg = d->n_q_seg;
+  a.n_kv_seg = d->n_kv_seg;
+  for (int i = 0; i < 2; ++i) {
+    const bool qv = i < d->n_q_seg, kvv = i < d->n_kv_seg;
+    a.qs[i] = {qv ? d->q_seg[i].start : 0, qv ? d->q_seg[i].len : 0, qv ? d->q_seg[i].stride : 1};
+    a.ks[i] = {kvv ? d->kv_seg[i].start : 0, kvv ? d->kv_seg[i].len : 0, kvv ? d->kv_seg[i].stride : 1};
+  }
+  return a;
+}
+
+int64_t pairs_of(const ra_step_desc* d) {
+  if (!d->causal) return d->q_len * d->kv_len;
+  int64_t total = 0;
+  for (int qi = 0; qi < d->n_q_seg; ++qi) {
+    const ra_segment& q = d->q_seg[qi];
+    for (int ki = 0; ki < d->n_kv_seg; ++ki) {
+      const ra_segment& k = d->kv_seg[ki];
+      if (q.len == 0 || k.len == 0) continue;
+      if (q.stride == 1) {
+        // rows whose count is clipped at 0, growing by one per row (stride-1
+        // keys), or saturated at k.len: sum in closed form by splitting the
+        // q range where count_le changes regime.
+        int64_t i = 0;
+        while (i < q.len) {
+          const int64_t x = q.start + i;
+          const int64_t c = count_le(k, x);
+          if (c == 0) {  // jump to the first row that sees key 0
+            const int64_t first = k.start - q.start;
+            if (first >= q.len) break;
+            i = first > i ? first : i + 1;
+            continue;
+          }
+          if (c == k.len) {
+            total += (q.len - i) * k.len;
+            break;
+          }
+          if (k.stride == 1) {
+            // c grows by 1 per row until it reaches k.len
+            const int64_t n = std::min(q.len - i, k.len - c);
+            total += n * c + n * (n - 1) / 2;
+            i += n;
+          } else {
+            total += c;
+            ++i;
+          }
+        }
+      } else {
+        for (int64_t i = 0; i < q.len; ++i) total += count_le(k, q.start + i * q.stride);
+      }
+    }
+  }
+  return total;
+}
+
+hipError_t launch_step(const ra::StepArgs& a, int head_dim, int dtype, hipStream_t s) {
+  if (a.q_len == 0 || a.batch == 0) return hipSuccess;
+  return dtype == RA_BF16 ? ra::launch_step_bf16(a, head_dim, s) : ra::launch_step_f32(a, head_dim, s);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct RingLayout {
+  size_t block_bytes;  // one K (or V) block
+  size_t state_rows;
+  size_t off_slot[2][2];
+  size_t off_o, off_m, off_l, total;
+};
+
+bool ring_layout(const ra_ring_desc* d, RingLayout* L) {
+  const size_t es = d->dtype == RA_BF16 ? 2 : 4;
+  L->block_bytes = (size_t)d->batch * d->heads_kv * (size_t)d->local_len * d->head_dim * es;
+  L->state_rows = (size_t)d->batch * d->heads_q * (size_t)d->local_len;
+  size_t off = 0;
+  for (int s = 0; s < 2; ++s)
+    for (int t = 0; t < 2; ++t) {
+      L->off_slot[s][t] = off;
+      off += align256(L->block_bytes);
+    }
+  L->off_o = off;
+  off += align256(L->state_rows * d->head_dim * 4);
+  L->off_m = off;
+  off += align256(L->state_rows * 4);
+  L->off_l = off;
+  off += align256(L->state_rows * 4);
+  L->total = off + 256;  // room to align the caller's base pointer
+  return true;
+}
+
+int check_ring_desc(const ra_ring_desc* d) {
+  if (d == nullptr) return fail(RA_ERR_INVALID_ARG, "ring desc is NULL");
+  if (d->world < 1) return fail(RA_ERR_INVALID_ARG, "world must be >= 1");
+  if (d->rank < 0 || d->rank >= d->world) return fail(RA_ERR_INVALID_ARG, "rank out of range");
+  if (d->partition < RA_PART_CONTIGUOUS || d->partition > RA_PART_STRIPED)
+    return fail(RA_ERR_INVALID_ARG, "unknown partition %d", d->partition);
+  if (d->local_len < 0 || d->local_len > kMaxRows) return fail(RA_ERR_INVALID_ARG, "local_len out of range");
+  if (d->partition == RA_PART_ZIGZAG && (d->local_len % 2) != 0)
+    return fail(RA_ERR_INVALID_ARG, "zigzag needs an even local_len");
+  if (d->reverse_order != 0 && d->reverse_order != 1) return fail(RA_ERR_INVALID_ARG, "reverse_order must be 0/1");
+  if (d->causal != 0 && d->causal != 1) return fail(RA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  ra_step_desc s{};
+  s.batch = d->batch;
+  s.heads_q = d->heads_q;
+  s.heads_kv = d->heads_kv;
+  s.head_dim = d->head_dim;
+  s.q_len = d->local_len;
+  s.kv_len = d->local_len;
+  s.dtype = d->dtype;
+  s.scale = d->scale;
+  return check_shape(&s, true);
+}
+
+int32_t owner_of(const ra_ring_desc* d, int32_t step) {
+  const int32_t n = d->world;
+  return d->reverse_order ? (d->rank + step) % n : ((d->rank - step) % n + n) % n;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ring_attn_last_error(void) { return g_last_error; }
+
+int32_t ring_attn_abi_version(void) { return 100; }
+
+int ring_attn_partition_segments(int32_t partition, int32_t world, int32_t rank, int64_t local_len,
+                                 ra_segment* segs, int32_t* n_segs) {
+  if (segs == nullptr || n_segs == nullptr) return fail(RA_ERR_INVALID_ARG, "segs/n_segs is NULL");
+  if (world < 1 || rank < 0 || rank >= world) return fail(RA_ERR_INVALID_ARG, "bad world/rank");
+  if (local_len < 0 || local_len > kMaxRows) return fail(RA_ERR_INVALID_ARG, "local_len out of range");
+  switch (partition) {
+    case RA_PART_CONTIGUOUS:
+      segs[0] = {(int64_t)rank * local_len, local_len, 1};
+      *n_segs = 1;
+      return RA_OK;
+    case RA_PART_ZIGZAG: {
+      if (local_len % 2) return fail(RA_ERR_INVALID_ARG, "zigzag needs an even local_len");
+      const int64_t g = local_len / 2;
+      segs[0] = {(int64_t)rank * g, g, 1};
+      segs[1] = {(int64_t)(2 * world - 1 - rank) * g, g, 1};
+      *n_segs = 2;
+      return RA_OK;
+    }
+    case RA_PART_STRIPED:
+      segs[0] = {(int64_t)rank, local_len, (int64_t)world};
+      *n_segs = 1;
+      return RA_OK;
+    default:
+      return fail(RA_ERR_INVALID_ARG, "unknown partition %d", partition);
+  }
+}
+
+int ring_attn_ring_step_desc(const ra_ring_desc* d, int32_t step, ra_step_desc* out, int32_t* owner) {
+  int rc = check_ring_desc(d);
+  if (rc) return rc;
+  if (out == nullptr) return fail(RA_ERR_INVALID_ARG, "out is NULL");
+  if (step < 0 || step >= d->world) return fail(RA_ERR_INVALID_ARG, "step out of range");
+  ra_step_desc s{};
+  s.batch = d->batch;
+  s.heads_q = d->heads_q;
+  s.heads_kv = d->heads_kv;
+  s.head_dim = d->head_dim;
+  s.q_len = d->local_len;
+  s.kv_len = d->local_len;
+  s.dtype = d->dtype;
+  s.causal = d->causal;
+  s.scale = d->scale;
+  const int32_t j = owner_of(d, step);
+  rc = ring_attn_partition_segments(d->partition, d->world, d->rank, d->local_len, s.q_seg, &s.n_q_seg);
+  if (rc) return rc;
+  rc = ring_attn_partition_segments(d->partition, d->world, j, d->local_len, s.kv_seg, &s.n_kv_seg);
+  if (rc) return rc;
+  *out = s;
+  if (owner) *owner = j;
+  return RA_OK;
+}
+
+int64_t ring_attn_visible_pairs(const ra_step_desc* d) {
+  if (check_step_desc(d) != RA_OK) return -1;
+  return pairs_of(d);
+}
+
+int ring_attn_step(const ra_step_desc* d, const void* q, const void* k, const void* v, float* o_acc, float* m,
+                   float* l, int32_t flags, void* stream) {
+  int rc = check_step_desc(d);
+  if (rc) return rc;
+  if (flags & ~RA_STEP_INIT) return fail(RA_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  const bool has_rows = d->q_len > 0 && d->batch > 0;
+  if (has_rows) {
+    if (!q || !o_acc || !m || !l) return fail(RA_ERR_INVALID_ARG, "q/o_acc/m/l must not be NULL");
+    if (d->kv_len > 0 && (!k || !v)) return fail(RA_ERR_INVALID_ARG, "k/v must not be NULL");
+    if (!aligned16(q) || !aligned16(o_acc) || (k && !aligned16(k)) || (v && !aligned16(v)))
+      return fail(RA_ERR_INVALID_ARG, "q/k/v/o_acc must be 16-byte aligned");
+  }
+  if (!has_rows) return RA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool init = flags & RA_STEP_INIT;
+  hipError_t e;
+  if (pairs_of(d) == 0) {
+    // no key of this block is visible to any row
+    if (!init) return RA_OK;
+    e = ra::launch_init_state(o_acc, m, l, (int64_t)d->batch * d->heads_q * d->q_len, d->head_dim, s);
+    return e == hipSuccess ? RA_OK : hip_fail(e, "init_state launch");
+  }
+  ra::StepArgs a = make_args(d);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o_acc;
+  a.m = m;
+  a.l = l;
+  a.init = init;
+  e = launch_step(a, d->head_dim, d->dtype, s);
+  return e == hipSuccess ? RA_OK : hip_fail(e, "step launch");
+}
+
+int ring_attn_merge(const ra_step_desc* d, float* o_a, float* m_a, float* l_a, const float* o_b, const float* m_b,
+                    const float* l_b, void* stream) {
+  int rc = check_shape(d, false);
+  if (rc) return rc;
+  const int64_t rows = (int64_t)d->batch * d->heads_q * d->q_len;
+  if (rows == 0) return RA_OK;
+  if (!o_a || !m_a || !l_a || !o_b || !m_b || !l_b) return fail(RA_ERR_INVALID_ARG, "state pointers must not be NULL");
+  if (!aligned16(o_a) || !aligned16(o_b)) return fail(RA_ERR_INVALID_ARG, "o_a/o_b must be 16-byte aligned");
+  hipError_t e = ra::launch_merge(o_a, m_a, l_a, o_b, m_b, l_b, rows, d->head_dim, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RA_OK : hip_fail(e, "merge launch");
+}
+
+int ring_attn_finalize(const ra_step_desc* d, const float* o_acc, const float* m, const float* l, void* out,
+                       float* lse, void* stream) {
+  int rc = check_shape(d, false);
+  if (rc) return rc;
+  const int64_t rows = (int64_t)d->batch * d->heads_q * d->q_len;
+  if (rows == 0) return RA_OK;
+  if (!o_acc || !m || !l || !out) return fail(RA_ERR_INVALID_ARG, "o_acc/m/l/out must not be NULL");
+  if (!aligned16(o_acc) || !aligned16(out)) return fail(RA_ERR_INVALID_ARG, "o_acc/out must be 16-byte aligned");
+  hipError_t e =
+      ra::launch_finalize(o_acc, m, l, out, lse, rows, d->head_dim, d->dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RA_OK : hip_fail(e, "finalize launch");
+}
+
+size_t ring_attn_forward_workspace_size(const ra_ring_desc* d) {
+  if (check_ring_desc(d) != RA_OK) return 0;
+  RingLayout L;
+  ring_layout(d, &L);
+  return L.total;
+}
+
+namespace {
+
+// Per-thread cache of the driver's synchronisation events (never timed).
+struct DriverEvents {
+  int device = -1;
+  hipEvent_t ready[2] = {nullptr, nullptr};  // slot filled (copy stream)
+  hipEvent_t freed[2] = {nullptr, nullptr};  // slot no longer read (compute stream)
+};
+thread_local DriverEvents g_events;
+
+hipError_t driver_events(DriverEvents** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  DriverEvents& ev = g_events;
+  if (ev.device != dev) {
+    for (int i = 0; i < 2; ++i) {
+      if ((e = hipEventCreateWithFlags(&ev.ready[i], hipEventDisableTiming)) != hipSuccess) return e;
+      if ((e = hipEventCreateWithFlags(&ev.freed[i], hipEventDisableTiming)) != hipSuccess) return e;
+    }
+    ev.device = dev;
+  }
+  *out = &ev;
+  return hipSuccess;
+}
+
+}  // namespace
+
+int ring_attn_forward(const ra_ring_desc* d, const void* q_local, const void* const* k_blocks,
+                      const void* const* v_blocks, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                      void* compute_stream, void* copy_stream, void* const* step_events) {
+  int rc = check_ring_desc(d);
+  if (rc) return rc;
+  const int n = d->world;
+  const bool has_rows = d->local_len > 0 && d->batch > 0;
+  if (!k_blocks || !v_blocks) return fail(RA_ERR_INVALID_ARG, "k_blocks/v_blocks must not be NULL");
+  if (has_rows) {
+    if (!q_local || !out) return fail(RA_ERR_INVALID_ARG, "q_local/out must not be NULL");
+    if (!aligned16(q_local) || !aligned16(out)) return fail(RA_ERR_INVALID_ARG, "q_local/out must be 16-byte aligned");
+    for (int j = 0; j < n; ++j) {
+      if (!k_blocks[j] || !v_blocks[j]) return fail(RA_ERR_INVALID_ARG, "block %d pointer is NULL", j);
+      if (!aligned16(k_blocks[j]) || !aligned16(v_blocks[j]))
+        return fail(RA_ERR_INVALID_ARG, "block %d is not 16-byte aligned", j);
+    }
+  }
+  if (step_events)
+    for (int i = 0; i < 2 * n; ++i)
+      if (!step_events[i]) return fail(RA_ERR_INVALID_ARG, "step_events[%d] is NULL", i);
+  RingLayout L;
+  ring_layout(d, &L);
+  if (workspace == nullptr || workspace_bytes < L.total)
+    return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, workspace_bytes);
+  if (copy_stream != nullptr && copy_stream == compute_stream)
+    return fail(RA_ERR_INVALID_ARG, "copy_stream must differ from compute_stream (or be NULL)");
+  if (!has_rows) return RA_OK;
+
+  // Plan the steps on the host: descriptors and which launch.
+  std::vector<ra_step_desc> steps(n);
+  std::vector<int32_t> owner(n);
+  std::vector<int64_t> pairs(n);
+  int first = -1, last = -1;
+  for (int s = 0; s < n; ++s) {
+    rc = ring_attn_ring_step_desc(d, s, &steps[s], &owner[s]);
+    if (rc) return rc;
+    pairs[s] = pairs_of(&steps[s]);
+    if (pairs[s] > 0) {
+      if (first < 0) first = s;
+      last = s;
+    }
+  }
+
+  char* base = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~(uintptr_t)255);
+  void* slot_k[2] = {base + L.off_slot[0][0], base + L.off_slot[1][0]};
+  void* slot_v[2] = {base + L.off_slot[0][1], base + L.off_slot[1][1]};
+  float* o = reinterpret_cast<float*>(base + L.off_o);
+  float* m = reinterpret_cast<float*>(base + L.off_m);
+  float* l = reinterpret_cast<float*>(base + L.off_l);
+
+  hipStream_t cs = static_cast<hipStream_t>(compute_stream);
+  hipStream_t xs = copy_stream ? static_cast<hipStream_t>(copy_stream) : cs;
+  DriverEvents* ev = nullptr;
+  hipError_t e = driver_events(&ev);
+  if (e != hipSuccess) return hip_fail(e, "event creation");
+  bool freed_recorded[2] = {false, false};
+
+  // The copy stream must not start before work already queued on the compute
+  // stream that produced the inputs: order it after the compute stream once.
+  if (xs != cs) {
+    if ((e = hipEventRecord(ev->freed[0], cs)) != hipSuccess) return hip_fail(e, "event record");
+    if ((e = hipStreamWaitEvent(xs, ev->freed[0], 0)) != hipSuccess) return hip_fail(e, "stream wait");
+  }
+
+  auto enqueue_receive = [&](int s) -> hipError_t {
+    // step s reads slot s%2; it was last read by step s-2
+    const int slot = s & 1;
+    hipError_t err;
+    if (freed_recorded[slot] && xs != cs)
+      if ((err = hipStreamWaitEvent(xs, ev->freed[slot], 0)) != hipSuccess) return err;
+    if ((err = hipMemcpyAsync(slot_k[slot], k_blocks[owner[s]], L.block_bytes, hipMemcpyDeviceToDevice, xs)) !=
+        hipSuccess)
+      return err;
+    if ((err = hipMemcpyAsync(slot_v[slot], v_blocks[owner[s]], L.block_bytes, hipMemcpyDeviceToDevice, xs)) !=
+        hipSuccess)
+      return err;
+    return hipEventRecord(ev->ready[slot], xs);
+  };
+
+  for (int s = 0; s < n; ++s) {
+    // receive the block of step s+1 while step s computes
+    if (s + 1 < n)
+      if ((e = enqueue_receive(s + 1)) != hipSuccess) return hip_fail(e, "receive copy");
+    const void* kb = k_blocks[owner[s]];
+    const void* vb = v_blocks[owner[s]];
+    if (s > 0) {
+      kb = slot_k[s & 1];
+      vb = slot_v[s & 1];
+      if (xs != cs)
+        if ((e = hipStreamWaitEvent(cs, ev->ready[s & 1], 0)) != hipSuccess) return hip_fail(e, "stream wait");
+    }
+    if (step_events)
+      if ((e = hipEventRecord(static_cast<hipEvent_t>(step_events[2 * s]), cs)) != hipSuccess)
+        return hip_fail(e, "step event");
+    if (pairs[s] > 0) {
+      ra::StepArgs a = make_args(&steps[s]);
+      a.q = q_local;
+      a.k = kb;
+      a.v = vb;
+      a.o = o;
+      a.m = m;
+      a.l = l;
+      a.init = (s == first);
+      a.final_ = (s == last);
+      a.out = out;
+      a.lse = lse;
+      if ((e = launch_step(a, d->head_dim, d->dtype, cs)) != hipSuccess) return hip_fail(e, "step launch");
+    }
+    if (step_events)
+      if ((e = hipEventRecord(static_cast<hipEvent_t>(step_events[2 * s + 1]), cs)) != hipSuccess)
+        return hip_fail(e, "step event");
+    if (s > 0 && xs != cs) {
+      if ((e = hipEventRecord(ev->freed[s & 1], cs)) != hipSuccess) return hip_fail(e, "event record");
+      freed_recorded[s & 1] = true;
+    }
+  }
+
+  if (last < 0) {
+    // no step saw any key: every row is empty
+    const int64_t rows = (int64_t)L.state_rows;
+    if ((e = ra::launch_init_state(o, m, l, rows, d->head_dim, cs)) != hipSuccess) return hip_fail(e, "init");
+    if ((e = ra::launch_finalize(o, m, l, out, lse, rows, d->head_dim, d->dtype, cs)) != hipSuccess)
+      return hip_fail(e, "finalize");
+  }
+  // The copy stream's last work is ordered before the compute stream's last
+  // step (which waited on it), so the caller only needs to sync compute_stream.
+  return RA_OK;
+}
+
+int ring_attn_events_create(int32_t n, void** events) {
+  if (n < 0 || (n > 0 && events == nullptr)) return fail(RA_ERR_INVALID_ARG, "bad event array");
+  for (int i = 0; i < n; ++i) {
+    hipEvent_t e;
+    hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) {
+      for (int j = 0; j < i; ++j) (void)hipEventDestroy(static_cast<hipEvent_t>(events[j]));
+      return hip_fail(err, "hipEventCreate");
+    }
+    events[i] = e;
+  }
+  return RA_OK;
+}
+
+int ring_attn_event_elapsed_ms(void* start, void* stop, float* ms) {
+  if (!start || !stop || !ms) return fail(RA_ERR_INVALID_ARG, "NULL argument");
+  hipError_t e = hipEventElapsedTime(ms, static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop));
+  return e == hipSuccess ? RA_OK : hip_fail(e, "hipEventElapsedTime");
+}
+
+int ring_attn_events_destroy(int32_t n, void* const* events) {
+  if (n < 0 || (n > 0 && events == nullptr)) return fail(RA_ERR_INVALID_ARG, "bad event array");
+  for (int i = 0; i < n; ++i)
+    if (events[i]) (void)hipEventDestroy(static_cast<hipEvent_t>(events[i]));
+  return RA_OK;
+}
+
+int ring_attn_synchronize(void* stream) {
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RA_OK : hip_fail(e, "hipStreamSynchronize");
+}
+
+}  // extern "C"

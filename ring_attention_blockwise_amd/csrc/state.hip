@@ -1,0 +1,140 @@
+// State kernels of the ring step: merge of two (O, m, l) states, finalize
+// (O / l and LSE), and the empty-state fill.
+//
+// Merge is the online-softmax fold of "distributed training hands-on code",
+// section 6.2 (block_attention: M' = max(M, M_b), L' = L e^(M-M') + ...,
+// O' = O e^(M-M') + ...) applied to two partial states; finalize is that
+// page's closing O / L plus the log-sum-exp. All three are HBM-bound
+// streaming passes: one workgroup of 256 threads handles 16 rows, 16 threads
+// per row, each thread moving 16-byte vectors along head_dim.
+#include "common.h"
+
+namespace ra {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kThreadsPerRow = 16;
+constexpr int kRowsPerBlock = kThreads / kThreadsPerRow;
+
+// Scale factor 2^(m_x - m) of one side of a merge, 0 for an empty side.
+__device__ __forceinline__ float side_weight(float mx, float m) {
+  return mx == -INFINITY ? 0.0f : exp2f(mx - m);
+}
+
+template <int D>
+__global__ void __launch_bounds__(kThreads) merge_kernel(float* __restrict__ o_a, float* __restrict__ m_a,
+                                                         float* __restrict__ l_a, const float* __restrict__ o_b,
+                                                         const float* __restrict__ m_b,
+                                                         const float* __restrict__ l_b, int64_t rows) {
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kThreadsPerRow;
+  const int sub = threadIdx.x % kThreadsPerRow;
+  if (row >= rows) return;
+  const float ma = m_a[row], mb = m_b[row];
+  const float m = fmaxf(ma, mb);
+  if (m == -INFINITY) return;  // both sides empty: a stays empty
+  const float wa = side_weight(ma, m), wb = side_weight(mb, m);
+  // Products rounded separately, then one add: the result is bitwise
+  // symmetric in (a, b).
+  float4* oa = reinterpret_cast<float4*>(o_a + row * D);
+  const float4* ob = reinterpret_cast<const float4*>(o_b + row * D);
+#pragma unroll
+  for (int i = sub; i < D / 4; i += kThreadsPerRow) {
+    float4 x = oa[i], y = ob[i];
+    x.x = __fadd_rn(__fmul_rn(wa, x.x), __fmul_rn(wb, y.x));
+    x.y = __fadd_rn(__fmul_rn(wa, x.y), __fmul_rn(wb, y.y));
+    x.z = __fadd_rn(__fmul_rn(wa, x.z), __fmul_rn(wb, y.z));
+    x.w = __fadd_rn(__fmul_rn(wa, x.w), __fmul_rn(wb, y.w));
+    oa[i] = x;
+  }
+  if (sub == 0) {
+    l_a[row] = __fadd_rn(__fmul_rn(wa, l_a[row]), __fmul_rn(wb, l_b[row]));
+    m_a[row] = m;
+  }
+}
+
+template <int D, bool BF16>
+__global__ void __launch_bounds__(kThreads) finalize_kernel(const float* __restrict__ o, const float* __restrict__ m,
+                                                            const float* __restrict__ l, void* __restrict__ out,
+                                                            float* __restrict__ lse, int64_t rows) {
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kThreadsPerRow;
+  const int sub = threadIdx.x % kThreadsPerRow;
+  if (row >= rows) return;
+  const float lr = l[row];
+  const float inv = finalize_inv(lr);
+  const float4* src = reinterpret_cast<const float4*>(o + row * D);
+#pragma unroll
+  for (int i = sub; i < D / 4; i += kThreadsPerRow) {
+    float4 x = src[i];
+    x.x *= inv;
+    x.y *= inv;
+    x.z *= inv;
+    x.w *= inv;
+    if constexpr (BF16) {
+      uint2 packed;
+      packed.x = (uint32_t)f32_to_bf16_bits(x.x) | ((uint32_t)f32_to_bf16_bits(x.y) << 16);
+      packed.y = (uint32_t)f32_to_bf16_bits(x.z) | ((uint32_t)f32_to_bf16_bits(x.w) << 16);
+      reinterpret_cast<uint2*>(static_cast<unsigned short*>(out) + row * D)[i] = packed;
+    } else {
+      reinterpret_cast<float4*>(static_cast<float*>(out) + row * D)[i] = x;
+    }
+  }
+  if (sub == 0 && lse != nullptr) lse[row] = finalize_lse(m[row], lr);
+}
+
+template <int D>
+__global__ void __launch_bounds__(kThreads) init_state_kernel(float* __restrict__ o, float* __restrict__ m,
+                                                              float* __restrict__ l, int64_t rows) {
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kThreadsPerRow;
+  const int sub = threadIdx.x % kThreadsPerRow;
+  if (row >= rows) return;
+  float4* dst = reinterpret_cast<float4*>(o + row * D);
+#pragma unroll
+  for (int i = sub; i < D / 4; i += kThreadsPerRow) dst[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (sub == 0) {
+    m[row] = -INFINITY;
+    l[row] = 0.0f;
+  }
+}
+
+inline dim3 grid_for(int64_t rows) { return dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)); }
+
+}  // namespace
+
+hipError_t launch_merge(float* o_a, float* m_a, float* l_a, const float* o_b, const float* m_b,
+                        const float* l_b, int64_t rows, int head_dim, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (head_dim == 128)
+    merge_kernel<128><<<grid_for(rows), kThreads, 0, s>>>(o_a, m_a, l_a, o_b, m_b, l_b, rows);
+  else
+    merge_kernel<64><<<grid_for(rows), kThreads, 0, s>>>(o_a, m_a, l_a, o_b, m_b, l_b, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const float* o, const float* m, const float* l, void* out, float* lse,
+                           int64_t rows, int head_dim, int dtype, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const dim3 g = grid_for(rows);
+  if (head_dim == 128) {
+    if (dtype == RA_BF16)
+      finalize_kernel<128, true><<<g, kThreads, 0, s>>>(o, m, l, out, lse, rows);
+    else
+      finalize_kernel<128, false><<<g, kThreads, 0, s>>>(o, m, l, out, lse, rows);
+  } else {
+    if (dtype == RA_BF16)
+      finalize_kernel<64, true><<<g, kThreads, 0, s>>>(o, m, l, out, lse, rows);
+    else
+      finalize_kernel<64, false><<<g, kThreads, 0, s>>>(o, m, l, out, lse, rows);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_init_state(float* o, float* m, float* l, int64_t rows, int head_dim, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (head_dim == 128)
+    init_state_kernel<128><<<grid_for(rows), kThreads, 0, s>>>(o, m, l, rows);
+  else
+    init_state_kernel<64><<<grid_for(rows), kThreads, 0, s>>>(o, m, l, rows);
+  return hipGetLastError();
+}
+
+}  // namespace ra

@@ -1,0 +1,161 @@
+"""Build one device's share of a ring workload on the GPU and run it.
+
+Inputs come from ``ring_inputs`` (seeded, chunk-indexed); rows are mapped to
+devices with the library's own partition map (ring_attn_partition_segments).
+Nothing here computes attention: the step, merge, finalize and the ring
+driver all run in libring_attn.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+import ring_inputs
+from . import (BF16, F32, RingDesc, finalize, forward, forward_workspace_size, partition_segments,
+               ring_desc, ring_step_desc, step, visible_pairs)
+
+
+def positions(segs) -> np.ndarray:
+    """Global positions of the rows described by [(start, len[, stride])]."""
+    if not segs:
+        return np.zeros(0, dtype=np.int64)
+    parts = []
+    for seg in segs:
+        start, n = seg[0], seg[1]
+        stride = seg[2] if len(seg) > 2 else 1
+        parts.append(np.arange(start, start + n * stride, stride, dtype=np.int64)[:n])
+    return np.concatenate(parts)
+
+
+def dtype_code(wl: ring_inputs.Workload) -> int:
+    return BF16 if wl.dtype == "bf16" else F32
+
+
+def torch_dtype(wl):
+    import torch
+    return torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+
+
+def make_ring_desc(wl: ring_inputs.Workload, rank: int, reverse_order: bool = False) -> RingDesc:
+    return ring_desc(wl.batch, wl.heads_q, wl.heads_kv, wl.head_dim, wl.local_len, wl.world, rank,
+                     wl.partition, dtype=dtype_code(wl), causal=wl.causal, reverse_order=reverse_order)
+
+
+@dataclasses.dataclass
+class DeviceShare:
+    workload: ring_inputs.Workload
+    rank: int
+    q: "object"                 # [B, Hq, c, d] on the GPU
+    k_blocks: list              # world tensors [B, Hkv, c, d]
+    v_blocks: list
+    q_positions: np.ndarray     # global position of each local row
+
+    def ring_desc(self, reverse_order=False) -> RingDesc:
+        return make_ring_desc(self.workload, self.rank, reverse_order)
+
+
+def _to_device(x: np.ndarray, dt, device):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device=device).to(dt)
+
+
+def build_share(wl: ring_inputs.Workload, rank: int, device, on_head=None) -> DeviceShare:
+    """Q of device ``rank`` and every device's K/V block, resident on ``device``.
+
+    ``on_head(b, g, k_f32, v_f32)``, if given, is called with each KV head's
+    whole global K/V (float32 numpy) as it is drawn, so callers can use the
+    same draw without holding every head at once.
+    """
+    import torch
+    dt = torch_dtype(wl)
+    B, Hq, Hk, d, c, n = wl.batch, wl.heads_q, wl.heads_kv, wl.head_dim, wl.local_len, wl.world
+    L = wl.total_len
+    qpos = positions(partition_segments(wl.partition, n, rank, c))
+    q = torch.empty((B, Hq, c, d), dtype=dt, device=device)
+    for b in range(B):
+        for h in range(Hq):
+            q[b, h] = _to_device(ring_inputs.rows(wl, "q", b, h, qpos), dt, device)
+    block_pos = [torch.from_numpy(positions(partition_segments(wl.partition, n, j, c))).to(device)
+                 for j in range(n)]
+    k_blocks = [torch.empty((B, Hk, c, d), dtype=dt, device=device) for _ in range(n)]
+    v_blocks = [torch.empty((B, Hk, c, d), dtype=dt, device=device) for _ in range(n)]
+    for b in range(B):
+        for g in range(Hk):
+            kh = ring_inputs.head(wl, "k", b, g)
+            vh = ring_inputs.head(wl, "v", b, g)
+            if on_head is not None:
+                on_head(b, g, kh, vh)
+            kd = _to_device(kh, dt, device)
+            vd = _to_device(vh, dt, device)
+            assert kd.shape[0] == L
+            for j in range(n):
+                k_blocks[j][b, g] = kd.index_select(0, block_pos[j])
+                v_blocks[j][b, g] = vd.index_select(0, block_pos[j])
+            del kd, vd
+    return DeviceShare(wl, rank, q, k_blocks, v_blocks, qpos)
+
+
+def alloc_outputs(share: DeviceShare):
+    import torch
+    wl = share.workload
+    out = torch.empty_like(share.q)
+    lse = torch.empty((wl.batch, wl.heads_q, wl.local_len), dtype=torch.float32, device=share.q.device)
+    return out, lse
+
+
+def alloc_workspace(share: DeviceShare, reverse_order=False):
+    import torch
+    n = forward_workspace_size(share.ring_desc(reverse_order))
+    return torch.empty(n, dtype=torch.uint8, device=share.q.device)
+
+
+def run_forward(share: DeviceShare, reverse_order=False, copy_stream=None, workspace=None, out=None, lse=None,
+                step_events=None):
+    """ring_attn_forward on the current stream (receive copies on ``copy_stream``)."""
+    if out is None:
+        out, lse = alloc_outputs(share)
+    if workspace is None:
+        workspace = alloc_workspace(share, reverse_order)
+    forward(share.ring_desc(reverse_order), share.q, share.k_blocks, share.v_blocks, out, lse, workspace,
+            copy_stream=copy_stream, step_events=step_events)
+    return out, lse
+
+
+def new_state(share: DeviceShare):
+    import torch
+    wl = share.workload
+    dev = share.q.device
+    o = torch.zeros((wl.batch, wl.heads_q, wl.local_len, wl.head_dim), dtype=torch.float32, device=dev)
+    m = torch.full((wl.batch, wl.heads_q, wl.local_len), float("-inf"), dtype=torch.float32, device=dev)
+    l = torch.zeros((wl.batch, wl.heads_q, wl.local_len), dtype=torch.float32, device=dev)
+    return o, m, l
+
+
+def run_steps(share: DeviceShare, steps, state=None, init_first=True):
+    """Apply ring steps (indices into the ring order) with ring_attn_step, in the given order."""
+    rd = share.ring_desc()
+    if state is None:
+        state = new_state(share)
+    o, m, l = state
+    first = init_first
+    for s in steps:
+        sd, owner = ring_step_desc(rd, s)
+        step(sd, share.q, share.k_blocks[owner], share.v_blocks[owner], o, m, l, init=first)
+        first = False
+    return o, m, l
+
+
+def finalize_state(share: DeviceShare, state):
+    rd = share.ring_desc()
+    sd, _ = ring_step_desc(rd, 0)
+    out, lse = alloc_outputs(share)
+    o, m, l = state
+    finalize(sd, o, m, l, out, lse)
+    return out, lse
+
+
+def step_pairs(wl: ring_inputs.Workload, rank: int):
+    """Visible (query, key) pairs per (batch, head) of every ring step of a share."""
+    rd = make_ring_desc(wl, rank)
+    return [visible_pairs(ring_step_desc(rd, s)[0]) for s in range(wl.world)]

@@ -1,0 +1,175 @@
+"""The C-ABI library on the host: it loads, exports every symbol the header
+declares, its host-only helpers agree with the oracle's independent code, and
+invalid arguments are rejected before any GPU work (nothing is launched)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import ring_attention_blockwise_amd as ra
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ring_attn.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ring_attn_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ra.lib()
+    names = _declared()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+    nm = subprocess.run(["nm", "-D", "--defined-only", ra.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (ring_attn_\w+)", nm))
+    assert set(names) <= exported
+    assert set(ra.EXPORTED) == set(names)
+
+
+def test_abi_version():
+    assert ra.lib().ring_attn_abi_version() == 100
+
+
+def _expand(segs):
+    return np.concatenate([np.arange(s, s + n * st, st) for s, n, st in segs]) if segs else np.zeros(0, int)
+
+
+@pytest.mark.parametrize("partition", ["contiguous", "zigzag", "striped"])
+@pytest.mark.parametrize("world,local", [(1, 8), (4, 16), (8, 1024), (64, 16384)])
+def test_partition_segments_match_oracle_positions(partition, world, local):
+    for rank in sorted({0, world // 2, world - 1}):
+        segs = ra.partition_segments(partition, world, rank, local)
+        np.testing.assert_array_equal(_expand(segs), oracle.device_positions(partition, world, rank, local))
+
+
+@pytest.mark.parametrize("partition", ["contiguous", "zigzag", "striped"])
+def test_visible_pairs_match_oracle_count(partition):
+    n, c = 8, 48
+    L = n * c
+    for rank in range(n):
+        for reverse in (False, True):
+            rd = ra.ring_desc(1, 2, 1, 64, c, n, rank, partition, reverse_order=reverse)
+            total = 0
+            for s in range(n):
+                sd, owner = ra.ring_step_desc(rd, s)
+                qp = oracle.device_positions(partition, n, rank, c)
+                kp = oracle.device_positions(partition, n, owner, c)
+                assert ra.visible_pairs(sd) == oracle.visible_pair_count(qp, kp, True)
+                total += ra.visible_pairs(sd)
+            assert total == oracle.visible_pair_count(oracle.device_positions(partition, n, rank, c),
+                                                      np.arange(L), True)
+
+
+def test_visible_pairs_random_segments():
+    rng = np.random.default_rng(0)
+    for _ in range(200):
+        segs_q = [(int(rng.integers(0, 50)), int(rng.integers(0, 20)), int(rng.integers(1, 4)))
+                  for _ in range(int(rng.integers(1, 3)))]
+        segs_k = [(int(rng.integers(0, 50)), int(rng.integers(0, 20)), int(rng.integers(1, 4)))
+                  for _ in range(int(rng.integers(1, 3)))]
+        nq = sum(s[1] for s in segs_q)
+        nk = sum(s[1] for s in segs_k)
+        sd = ra.step_desc(1, 1, 1, 64, nq, nk, causal=True, q_segs=segs_q, kv_segs=segs_k)
+        assert ra.visible_pairs(sd) == oracle.visible_pair_count(_expand(segs_q), _expand(segs_k), True)
+    sd = ra.step_desc(1, 1, 1, 64, 7, 5, causal=False)
+    assert ra.visible_pairs(sd) == 35
+
+
+def test_ring_step_owner_order():
+    rd = ra.ring_desc(1, 1, 1, 64, 16, 4, 1)
+    assert [ra.ring_step_desc(rd, s)[1] for s in range(4)] == [1, 0, 3, 2]
+    rd = ra.ring_desc(1, 1, 1, 64, 16, 4, 1, reverse_order=True)
+    assert [ra.ring_step_desc(rd, s)[1] for s in range(4)] == [1, 2, 3, 0]
+
+
+def test_workspace_size_covers_slots_and_state():
+    rd = ra.ring_desc(1, 32, 8, 128, 16384, 8, 0)
+    ws = ra.forward_workspace_size(rd)
+    block = 8 * 16384 * 128 * 2
+    state = 32 * 16384 * (128 * 4 + 8)
+    assert 4 * block + state <= ws <= 4 * block + state + 8 * 256
+
+
+# ---- validation: errors come back before anything is enqueued -------------------
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced on the host
+
+
+def _step_rc(sd, ptrs=(FAKE,) * 6, flags=0):
+    return ra.lib().ring_attn_step(ctypes.byref(sd), *ptrs, flags, None)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("head_dim", 96, ra.ERR_UNSUPPORTED), ("dtype", 7, ra.ERR_UNSUPPORTED),
+    ("heads_kv", 3, ra.ERR_INVALID_ARG), ("heads_q", 0, ra.ERR_INVALID_ARG),
+    ("batch", -1, ra.ERR_INVALID_ARG), ("q_len", -5, ra.ERR_INVALID_ARG),
+    ("causal", 2, ra.ERR_INVALID_ARG), ("scale", float("nan"), ra.ERR_INVALID_ARG),
+])
+def test_step_rejects_bad_descriptor(field, value, code):
+    sd = ra.step_desc(1, 4, 2, 128, 16, 16, q_segs=[(0, 16)], kv_segs=[(0, 16)])
+    setattr(sd, field, value)
+    assert _step_rc(sd) == code
+    assert ra.last_error() != ""
+
+
+def test_step_rejects_bad_segments_and_pointers():
+    sd = ra.step_desc(1, 1, 1, 64, 16, 16, q_segs=[(0, 15)], kv_segs=[(0, 16)])
+    assert _step_rc(sd) == ra.ERR_INVALID_ARG and "add up" in ra.last_error()
+    sd = ra.step_desc(1, 1, 1, 64, 16, 16, q_segs=[(0, 16, 0)], kv_segs=[(0, 16)])
+    assert _step_rc(sd) == ra.ERR_INVALID_ARG
+    sd = ra.step_desc(1, 1, 1, 64, 16, 16, causal=True)          # causal without positions
+    assert _step_rc(sd) == ra.ERR_INVALID_ARG
+    sd = ra.step_desc(1, 1, 1, 64, 16, 16, q_segs=[(0, 16)], kv_segs=[(0, 16)])
+    assert _step_rc(sd, (None,) + (FAKE,) * 5) == ra.ERR_INVALID_ARG
+    assert _step_rc(sd, (ctypes.c_void_p(0x10004),) + (FAKE,) * 5) == ra.ERR_INVALID_ARG  # misaligned
+    assert _step_rc(sd, flags=4) == ra.ERR_INVALID_ARG
+    empty = ra.step_desc(1, 1, 1, 64, 0, 16, q_segs=[(0, 0)], kv_segs=[(0, 16)])
+    assert _step_rc(empty, (None,) * 6) == ra.OK                 # no rows: nothing to do
+
+
+def test_merge_finalize_reject_bad_arguments():
+    L = ra.lib()
+    sd = ra.step_desc(1, 1, 1, 96, 16, 16, causal=False)
+    assert L.ring_attn_merge(ctypes.byref(sd), *(FAKE,) * 6, None) == ra.ERR_UNSUPPORTED
+    assert L.ring_attn_finalize(ctypes.byref(sd), *(FAKE,) * 5, None) == ra.ERR_UNSUPPORTED
+    sd = ra.step_desc(1, 1, 1, 64, 16, 16, causal=False)
+    assert L.ring_attn_merge(ctypes.byref(sd), None, *(FAKE,) * 5, None) == ra.ERR_INVALID_ARG
+    assert L.ring_attn_finalize(ctypes.byref(sd), FAKE, FAKE, FAKE, None, None, None) == ra.ERR_INVALID_ARG
+
+
+def test_forward_rejects_small_workspace_and_bad_desc():
+    L = ra.lib()
+    rd = ra.ring_desc(1, 2, 1, 64, 16, 4, 0)
+    blocks = (ctypes.c_void_p * 4)(*([0x10000] * 4))
+    ws = ra.forward_workspace_size(rd)
+    rc = L.ring_attn_forward(ctypes.byref(rd), FAKE, blocks, blocks, FAKE, FAKE, FAKE, ws - 1, None, None, None)
+    assert rc == ra.ERR_WORKSPACE
+    rc = L.ring_attn_forward(ctypes.byref(rd), FAKE, blocks, blocks, FAKE, FAKE, None, ws, None, None, None)
+    assert rc == ra.ERR_WORKSPACE
+    bad = ra.ring_desc(1, 2, 1, 64, 15, 4, 0, partition="zigzag")   # odd local length
+    assert L.ring_attn_forward(ctypes.byref(bad), FAKE, blocks, blocks, FAKE, FAKE, FAKE, ws, None, None,
+                               None) == ra.ERR_INVALID_ARG
+    bad = ra.ring_desc(1, 2, 1, 64, 16, 4, 4)                      # rank out of range
+    assert ra.lib().ring_attn_forward_workspace_size(ctypes.byref(bad)) == 0
+    nulls = (ctypes.c_void_p * 4)(*([0x10000] * 3 + [None]))
+    assert L.ring_attn_forward(ctypes.byref(rd), FAKE, blocks, nulls, FAKE, FAKE, FAKE, ws, None, None,
+                               None) == ra.ERR_INVALID_ARG
+    same = ctypes.c_void_p(0x5000)
+    assert L.ring_attn_forward(ctypes.byref(rd), FAKE, blocks, blocks, FAKE, FAKE, FAKE, ws, same, same,
+                               None) == ra.ERR_INVALID_ARG
+
+
+def test_partition_rejects_bad_input():
+    with pytest.raises(ra.RingAttnError):
+        ra.partition_segments("zigzag", 4, 0, 15)
+    with pytest.raises(ra.RingAttnError):
+        ra.partition_segments("contiguous", 4, 4, 16)
+    with pytest.raises(KeyError):
+        ra.partition_segments("diagonal", 4, 0, 16)
