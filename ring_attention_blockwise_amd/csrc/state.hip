@@ -26,6 +26,9 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(float* __restrict__ o_a
                                                          float* __restrict__ l_a, const float* __restrict__ o_b,
                                                          const float* __restrict__ m_b,
                                                          const float* __restrict__ l_b, int64_t rows) {
+  // Both products are rounded before the single add (no FMA contraction), so
+  // the result is bitwise symmetric in (a, b).
+#pragma clang fp contract(off)
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kThreadsPerRow;
   const int sub = threadIdx.x % kThreadsPerRow;
   if (row >= rows) return;
@@ -33,21 +36,19 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(float* __restrict__ o_a
   const float m = fmaxf(ma, mb);
   if (m == -INFINITY) return;  // both sides empty: a stays empty
   const float wa = side_weight(ma, m), wb = side_weight(mb, m);
-  // Products rounded separately, then one add: the result is bitwise
-  // symmetric in (a, b).
   float4* oa = reinterpret_cast<float4*>(o_a + row * D);
   const float4* ob = reinterpret_cast<const float4*>(o_b + row * D);
 #pragma unroll
   for (int i = sub; i < D / 4; i += kThreadsPerRow) {
     float4 x = oa[i], y = ob[i];
-    x.x = __fadd_rn(__fmul_rn(wa, x.x), __fmul_rn(wb, y.x));
-    x.y = __fadd_rn(__fmul_rn(wa, x.y), __fmul_rn(wb, y.y));
-    x.z = __fadd_rn(__fmul_rn(wa, x.z), __fmul_rn(wb, y.z));
-    x.w = __fadd_rn(__fmul_rn(wa, x.w), __fmul_rn(wb, y.w));
+    x.x = wa * x.x + wb * y.x;
+    x.y = wa * x.y + wb * y.y;
+    x.z = wa * x.z + wb * y.z;
+    x.w = wa * x.w + wb * y.w;
     oa[i] = x;
   }
   if (sub == 0) {
-    l_a[row] = __fadd_rn(__fmul_rn(wa, l_a[row]), __fmul_rn(wb, l_b[row]));
+    l_a[row] = wa * l_a[row] + wb * l_b[row];
     m_a[row] = m;
   }
 }
