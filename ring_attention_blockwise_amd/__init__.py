@@ -15,7 +15,7 @@ import os
 from typing import Optional, Sequence
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libring_attn.so")
+LIB_PATH = os.environ.get("RING_ATTN_LIB") or os.path.join(_HERE, "libring_attn.so")
 
 # ---- constants mirrored from ring_attn.h ------------------------------------
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4

@@ -6,29 +6,36 @@
 // Parallelism", sections 4/6 and lecture 30, section 3.2, and GQA head
 // sharing (lecture 30, section 3.4).
 //
-// Mapping (all sizes for head_dim D in {64, 128}):
-//  * A workgroup of 4 waves owns 128 query rows of one (batch, q head); each
-//    wave owns 32 rows. Workgroups that read the same KV head are placed on
-//    the same XCD (consecutive workgroup ids go round-robin over the 8 XCDs),
-//    and heavy causal tiles are dispatched first.
+// Mapping (head_dim D in {64, 128}):
+//  * A workgroup of 8 waves owns 256 query rows of one (batch, q head); each
+//    wave owns 32 rows. Waves w and w+4 run on the same SIMD. The two groups
+//    (waves 0-3 and 4-7) are kept one phase apart by a workgroup barrier at
+//    every phase boundary: while one wave of a SIMD issues its matrix
+//    instructions (P V of tile t-1 and S of tile t), its partner runs the
+//    softmax of its own tile on the vector ALUs, so the MFMA pipe and the
+//    VALU of each SIMD work at the same time ("ping-pong").
 //  * Keys are consumed in tiles of 64. K and V tiles are copied HBM -> LDS by
-//    16-byte direct-to-LDS loads (no register staging), double-buffered, one
-//    barrier per tile; an XOR swizzle of the 16-byte units of each row is
-//    applied through the global address so the LDS reads below are free of
-//    bank conflicts.
+//    16-byte buffer-to-LDS loads (bounds-checked by the buffer resource: rows
+//    past the block read as zero and are masked), in a ring of three LDS
+//    stages: a tile is loaded two phases before its first use.
+//  * The 16-byte units of each LDS row are XOR-swizzled through the global
+//    offset, so the K reads (16 lanes x 16 B over 16 rows) and the V
+//    transposed reads (4 rows x 4 units per half-wave) are free of bank
+//    conflicts.
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: K (A operand) is read with ds_read_b128, Q^T
 //    (B operand) sits in VGPRs for the whole launch. In the accumulator every
-//    lane then holds 32 keys of ONE query row, so the row max and row sum are
+//    lane holds 32 keys of ONE query row, so row max and row sum are
 //    lane-local plus one v_permlane32_swap with the partner lane.
 //  * P^T is converted to bf16 in registers and is directly the B operand of
 //    O^T += V^T P^T: the 32x32 accumulator layout puts keys {0-3, 8-11}+4h of
-//    each 16-key chunk in lane half h, and V^T (A operand) is fetched with the
-//    same key order by ds_read_b64_tr_b16 from row-major V, so no LDS round
-//    trip of P and no separate V transpose is needed.
+//    each 16-key chunk in lane half h, and V^T (A operand) is fetched in the
+//    same key order by ds_read_b64_tr_b16 from row-major V.
 //  * Softmax runs in base 2 with scale*log2(e) folded into one FMA per score.
 //    The reference maximum is raised lazily (only when a row's maximum grows
-//    by more than 2^8); O and l are rescaled only then, for the whole wave.
+//    by more than 8 in base-2 units); O and l are rescaled only then.
+#include <type_traits>
+
 #include "common.h"
 
 namespace ra {
@@ -40,27 +47,33 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;               // two groups of four; w and w+4 share a SIMD
 constexpr int kThreads = kWaves * 64;
-constexpr int kBM = kWaves * 32;  // query rows per workgroup
-constexpr int kBN = 64;           // keys per tile
+constexpr int kBM = kWaves * 32;        // query rows per workgroup
+constexpr int kBN = 64;                 // keys per tile
+constexpr int kStages = 3;              // LDS ring of K/V tiles
+#ifndef RA_LOOKAHEAD
+#define RA_LOOKAHEAD 6
+#endif
+constexpr int kLookahead = RA_LOOKAHEAD;  // MFMAs whose LDS operands are in flight
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer resource, dword access
 
 template <int D>
 struct Layout {
-  static constexpr int kRowBytes = D * 2;                       // one K or V row in LDS
-  static constexpr int kUnits = D / 8;                          // 16-byte units per row
-  static constexpr int kTileBytes = kBN * kRowBytes;            // one K (or V) tile
-  static constexpr int kLoadsPerWave = kTileBytes / 1024 / kWaves;  // 1 KB per wave load
-  static constexpr int kSmemBytes = 4 * kTileBytes;             // 2 buffers x (K, V)
-  static constexpr int kDChunks = D / 16;                       // K=16 steps of QK^T
-  static constexpr int kDBlocks = D / 32;                       // 32-row blocks of O^T
+  static constexpr int kRowBytes = D * 2;                        // one K or V row
+  static constexpr int kUnits = D / 8;                           // 16-byte units per row
+  static constexpr int kTileBytes = kBN * kRowBytes;             // one K (or V) tile
+  static constexpr int kVBase = kStages * kTileBytes;           // K stages, then V stages
+  static constexpr int kSmemBytes = 2 * kStages * kTileBytes;
+  static constexpr int kLoadsPerWave = kTileBytes / 1024 / kWaves;  // 1 KB per wave-wide load
+  static constexpr int kDChunks = D / 16;                        // K=16 steps of S^T
+  static constexpr int kDBlocks = D / 32;                        // 32-row blocks of O^T
+  static_assert(kLoadsPerWave >= 1, "tile too small for the wave count");
 
-  // Stored position of logical 16-byte unit c of row `row`.
-  // K rows are read 16 lanes x 16 B at a time over 16 consecutive rows;
-  // V rows are read by the transposing 8-byte reads over 4 consecutive rows.
+  // Stored position of logical 16-byte unit c of row `row` is c ^ swz(row).
   __device__ static __forceinline__ int k_swz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
   __device__ static __forceinline__ int v_swz(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
 };
@@ -91,32 +104,88 @@ __device__ __forceinline__ bf16x8 pack_p(const f32x16& s, int base) {
   return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Copy one K or V tile (64 rows starting at local key `start`) into LDS.
-// The wave's i-th load writes 1 KB of LDS at unit block (wave*L + i)*64; lane
-// `lane` of it fills stored unit p of row `row`, fetching logical unit
-// p ^ swz(row) from HBM. Rows past the end of the block are clamped to the
-// last row (their scores are masked).
-template <int D, bool IS_K>
-__device__ __forceinline__ void load_tile(const unsigned short* __restrict__ src, int64_t kv_len, int32_t start,
-                                          char* lds_tile, int wave, int lane) {
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over `nbytes` bytes at `base` (wave-uniform).
+__device__ __forceinline__ i32x4 buffer_resource(const void* base, int nbytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));  // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane(nbytes);
+  r[3] = kBufferWord3;
+  return r;
+}
+
+template <class T>
+__device__ __forceinline__ const __attribute__((address_space(3))) T* lds_ptr(uint32_t addr) {
+  return (const __attribute__((address_space(3))) T*)(uintptr_t)addr;
+}
+
+// One 16-byte-per-lane buffer load straight into LDS: lane i's 16 bytes land
+// at LDS byte address lds_base + 16*i. Issued through asm so the compiler
+// does not order later LDS reads of *other* stages behind it; the kernel
+// waits for it explicitly (vmcnt) before the barrier that publishes a tile.
+// M0 (the LDS destination) is saved and restored around the load.
+__device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t lds_base, int voff) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_base), "v"(voff), "s"(rsrc)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Copy the K and V tile of 64 rows starting at local key `start` into one LDS
+// stage. The buffer resources bound the reads to the rows the block has: rows
+// past kv_len read as zero (their scores are masked).
+template <int D>
+__device__ __forceinline__ void issue_tile(const char* kg, const char* vg, int64_t kv_len, int32_t start,
+                                           uint32_t k_dst, uint32_t v_dst, int wave, int lane) {
   using Ly = Layout<D>;
+  const int64_t left = kv_len - start;
+  const int nbytes = (int)((left < kBN ? left : kBN) * Ly::kRowBytes);
+  const i32x4 rk = buffer_resource(kg + (int64_t)start * Ly::kRowBytes, nbytes);
+  const i32x4 rv = buffer_resource(vg + (int64_t)start * Ly::kRowBytes, nbytes);
 #pragma unroll
   for (int i = 0; i < Ly::kLoadsPerWave; ++i) {
-    const int blk = wave * Ly::kLoadsPerWave + i;
-    const int u = blk * 64 + lane;
-    const int row = u / Ly::kUnits;
+    // lane fills stored unit p of row r and fetches logical unit p ^ swz(r)
+    const int u = (wave * Ly::kLoadsPerWave + i) * 64 + lane;
+    const int r = u / Ly::kUnits;
     const int p = u % Ly::kUnits;
-    const int c = p ^ (IS_K ? Ly::k_swz(row) : Ly::v_swz(row));
-    int64_t key = (int64_t)start + row;
-    key = key < kv_len ? key : kv_len - 1;
-    const unsigned short* g = src + key * D + c * 8;
-    __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds_tile + blk * 1024), 16, 0, 0);
+    const uint32_t blk = (uint32_t)((wave * Ly::kLoadsPerWave + i) * 1024);
+    dma16(rk, k_dst + blk, r * Ly::kRowBytes + ((p ^ Ly::k_swz(r)) << 4));
+    dma16(rv, v_dst + blk, r * Ly::kRowBytes + ((p ^ Ly::v_swz(r)) << 4));
   }
 }
 
+// Scheduling shape of a block of N MFMAs that each take R LDS reads: the
+// reads run four MFMAs ahead of their use (enough to cover LDS latency)
+// instead of all being hoisted up front, which would exhaust the registers.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+template <int N, int R, int AHEAD>
+__device__ __forceinline__ void pipeline_lds_mfma() {
+  constexpr int kAhead = AHEAD < N ? AHEAD : N - 1;
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kAhead * R, 0);
+#pragma unroll
+  for (int i = 0; i < N - kAhead; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, R, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, kAhead, 0);
+}
+
 template <int D>
-__global__ void __launch_bounds__(kThreads, 2) step_bf16_kernel(StepArgs a, int32_t n_items, int32_t items_per_xcd,
-                                                                int32_t q_tiles) {
+__global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t n_items, int32_t items_per_xcd,
+                                                             int32_t q_tiles) {
   using Ly = Layout<D>;
   __shared__ __attribute__((aligned(1024))) char smem[Ly::kSmemBytes];
 
@@ -132,10 +201,11 @@ __global__ void __launch_bounds__(kThreads, 2) step_bf16_kernel(StepArgs a, int3
   const int32_t h = kvh * a.group + rem % a.group;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int qcol = lane & 31;
   const int hh = lane >> 5;
+  const int group = wave >> 2;  // 0: first phase group, 1: one phase behind
 
   const int64_t row0 = (int64_t)tile * kBM;
   const int64_t r1 = (row0 + kBM < a.q_len) ? row0 + kBM : a.q_len;
@@ -151,18 +221,15 @@ __global__ void __launch_bounds__(kThreads, 2) step_bf16_kernel(StepArgs a, int3
   const int64_t bh = (int64_t)b * a.heads_q + h;
   const size_t srow = (size_t)(bh * a.q_len + rowc);
   const int64_t kv_off = ((int64_t)b * a.heads_kv + kvh) * a.kv_len * D;
-  const unsigned short* kg = static_cast<const unsigned short*>(a.k) + kv_off;
-  const unsigned short* vg = static_cast<const unsigned short*>(a.v) + kv_off;
+  const char* kg = reinterpret_cast<const char*>(static_cast<const unsigned short*>(a.k) + kv_off);
+  const char* vg = reinterpret_cast<const char*>(static_cast<const unsigned short*>(a.v) + kv_off);
 
-  // ---- start the first tile's copy as early as possible ----------------------
   auto tile_start = [&](int t) -> int32_t {
     return t < plan.r0.ntiles ? plan.r0.begin + t * kBN : plan.r1.begin + (t - plan.r0.ntiles) * kBN;
   };
-  if (ntiles > 0) {
-    const int32_t st = tile_start(0);
-    load_tile<D, true>(kg, a.kv_len, st, smem, wave, lane);
-    load_tile<D, false>(vg, a.kv_len, st, smem + Ly::kTileBytes, wave, lane);
-  }
+
+  const uint32_t smem_base = lds_address(smem);
+  if (ntiles > 0) issue_tile<D>(kg, vg, a.kv_len, tile_start(0), smem_base, smem_base + Ly::kVBase, wave, lane);
 
   // ---- Q^T fragments (B operand of S^T = K Q^T) ------------------------------
   bf16x8 qf[Ly::kDChunks];
@@ -204,115 +271,162 @@ __global__ void __launch_bounds__(kThreads, 2) step_bf16_kernel(StepArgs a, int3
   const int32_t vend1 = row_visible_end(a, plan.r1, qpos);
   const float sl2 = a.scale_log2;
 
+  // Per-lane LDS addresses, fixed for the launch; every read below adds only a
+  // compile-time offset (stage, key block, slice) that fits the 16-bit
+  // offset field of the instruction.
   // K read (A operand of S^T): row kb*32 + qcol, logical unit 2c + hh.
   const int k_swz = Ly::k_swz(qcol);
+  uint32_t k_addr[Ly::kDChunks];
+#pragma unroll
+  for (int c = 0; c < Ly::kDChunks; ++c)
+    k_addr[c] = smem_base + qcol * Ly::kRowBytes + (((2 * c + hh) ^ k_swz) << 4);
   // V^T read by ds_read_b64_tr_b16: within each 16-lane group, source lane
   // s = 4t + q points at row (4*hh + t) of the 8-row slice and at head_dim
-  // offset 32*db + 16*(group & 1) + 4q; the instruction hands output lane j
+  // offset 32*db + 16*(group16 & 1) + 4q; the instruction hands output lane j
   // element j%4 of source lane 4t + j/4, i.e. V[row t][d = ... + j].
-  const int grp = lane >> 4;
+  const int grp16 = lane >> 4;
   const int t4 = (lane & 15) >> 2;
   const int q4 = lane & 3;
   const int v_row = 4 * hh + t4;
   const int v_swz = Ly::v_swz(v_row);
-  int v_off[Ly::kDBlocks];
+  uint32_t v_addr[Ly::kDBlocks];
 #pragma unroll
   for (int db = 0; db < Ly::kDBlocks; ++db) {
-    const int unit = 4 * db + 2 * (grp & 1) + (q4 >> 1);
-    v_off[db] = v_row * Ly::kRowBytes + ((unit ^ v_swz) << 4) + ((q4 & 1) << 3);
+    const int unit = 4 * db + 2 * (grp16 & 1) + (q4 >> 1);
+    v_addr[db] = smem_base + Ly::kVBase + v_row * Ly::kRowBytes + ((unit ^ v_swz) << 4) + ((q4 & 1) << 3);
   }
 
-  for (int t = 0; t < ntiles; ++t) {
-    const bool first_range = t < plan.r0.ntiles;
-    const int32_t start = tile_start(t);
-    char* kt = smem + (t & 1) * 2 * Ly::kTileBytes;
-    char* vt = kt + Ly::kTileBytes;
+  f32x16 sacc[2];
+  bf16x8 pf[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sacc[kb][j] = 0.0f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) pf[kb][c] = bf16x8{};
 
-    // tile t has landed in LDS for every wave
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // Per wave the work is the sequence M_0 S_0 M_1 S_1 ... S_{n-1} M_n with
+  // M_v = (P V of tile v-1, S of tile v) on the matrix cores and S_t the
+  // softmax of tile t. Group 0 runs item i in phase i, group 1 in phase i+1;
+  // every phase ends at a workgroup barrier, so all waves pass 2n+2 barriers.
+  // At the start of even phase 2u tile u has landed (it was issued in phase
+  // 2u-2) and tile u+1 is issued into the stage tile u-2 used, whose last
+  // reader finished in phase 2u-1. Tile t lives in stage t % 3; the tile loop
+  // is unrolled by three so that stage is a compile-time constant.
+  int ph = 0;
+  auto next_phase = [&]() {
+    const int u = ph >> 1;
+    const bool even = (ph & 1) == 0;
+    if (even && u < ntiles) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (t + 1 < ntiles) {
-      // the other buffer was last read in iteration t-1, before the barrier
-      char* kn = smem + ((t + 1) & 1) * 2 * Ly::kTileBytes;
-      const int32_t sn = tile_start(t + 1);
-      load_tile<D, true>(kg, a.kv_len, sn, kn, wave, lane);
-      load_tile<D, false>(vg, a.kv_len, sn, kn + Ly::kTileBytes, wave, lane);
+    if (even && u + 1 < ntiles) {
+      const uint32_t st = (uint32_t)((u + 1) % kStages) * Ly::kTileBytes;
+      issue_tile<D>(kg, vg, a.kv_len, tile_start(u + 1), smem_base + st, smem_base + Ly::kVBase + st, wave, lane);
     }
+    ++ph;
+  };
 
-    // ---- S^T = K Q^T for two 32-key blocks --------------------------------
-    f32x16 sacc[2];
+  // One loop iteration: M_v (P V of tile v-1 from stage ST_PREV, S of tile v
+  // from stage ST), then S_v.
+  auto iteration = [&](auto st_tag, int v) {
+    constexpr int ST = decltype(st_tag)::value;
+    constexpr int ST_PREV = (ST + kStages - 1) % kStages;
+    next_phase();
+    if (v >= 1) {
+      // ---- O^T += V^T P^T for tile v-1 --------------------------------------
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) sacc[kb][j] = 0.0f;
-      const char* krow = kt + (kb * 32 + qcol) * Ly::kRowBytes;
+        for (int c = 0; c < 2; ++c) {
 #pragma unroll
-      for (int c = 0; c < Ly::kDChunks; ++c) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + (((2 * c + hh) ^ k_swz) << 4));
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sacc[kb], 0, 0, 0);
+          for (int db = 0; db < Ly::kDBlocks; ++db) {
+            constexpr int base = ST_PREV * Ly::kTileBytes;
+            const int slice = base + (kb * 32 + 16 * c) * Ly::kRowBytes;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)lds_ptr<s16x4>(v_addr[db] + slice));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)lds_ptr<s16x4>(v_addr[db] + slice + 8 * Ly::kRowBytes));
+            const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pf[kb][c],
+                                                               oacc[db], 0, 0, 0);
+          }
+        }
+      pipeline_lds_mfma<4 * Ly::kDBlocks, 2, kLookahead>();
+    }
+    if (v < ntiles) {
+      // ---- S^T = K Q^T for tile v, two 32-key blocks ----------------------------
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sacc[kb][j] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < Ly::kDChunks; ++c) {
+          const bf16x8 kf = *lds_ptr<bf16x8>(k_addr[c] + ST * Ly::kTileBytes + kb * 32 * Ly::kRowBytes);
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sacc[kb], 0, 0, 0);
+        }
       }
-    }
-
-    // ---- causal / ragged mask on partial tiles ---------------------------------
-    if (start + kBN > (first_range ? plan.r0.full : plan.r1.full)) {
-      const int32_t lim = (first_range ? vend0 : vend1) - start;  // keys [0, lim) of this tile are visible
+      pipeline_lds_mfma<2 * Ly::kDChunks, 1, kLookahead>();
+      next_phase();
+      // ---- softmax of tile v -------------------------------------------------------
+      const bool first_range = v < plan.r0.ntiles;
+      const int32_t start = tile_start(v);
+      if (start + kBN > (first_range ? plan.r0.full : plan.r1.full)) {
+        const int32_t lim = (first_range ? vend0 : vend1) - start;  // keys [0, lim) are visible
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int key = kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
+            if (key >= lim) sacc[kb][j] = -INFINITY;
+          }
+      }
+      float mx = sacc[0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kb][j]);
+      mx = max_with_partner(mx) * sl2;
+      const float cand = fmaxf(m_run, mx);
+      const bool need = cand > m_run + kRescaleThreshold;
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        const float m_upd = need ? cand : m_run;
+        const float alpha = (m_upd == m_run) ? 1.0f : exp2f(m_run - m_upd);
+#pragma unroll
+        for (int db = 0; db < Ly::kDBlocks; ++db)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
+        l_run *= alpha;
+        m_run = m_upd;
+      }
+      const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
+      float psum = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const int key = kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
-          if (key >= lim) sacc[kb][j] = -INFINITY;
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][j], sl2, -msub));
+          sacc[kb][j] = p;
+          psum += p;
         }
+      l_run += psum;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) pf[kb][c] = pack_p(sacc[kb], 8 * c);
     }
+  };
 
-    // ---- online softmax (base 2, lazy rescale) ------------------------------------
-    float mx = sacc[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kb][j]);
-    mx = max_with_partner(mx) * sl2;
-    const float cand = fmaxf(m_run, mx);
-    const bool need = cand > m_run + kRescaleThreshold;
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-      const float m_upd = need ? cand : m_run;
-      const float alpha = (m_upd == m_run) ? 1.0f : exp2f(m_run - m_upd);
-#pragma unroll
-      for (int db = 0; db < Ly::kDBlocks; ++db)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
-      l_run *= alpha;
-      m_run = m_upd;
-    }
-    const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
-    float psum = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][j], sl2, -msub));
-        sacc[kb][j] = p;
-        psum += p;
-      }
-    l_run += psum;
-
-    // ---- O^T += V^T P^T ------------------------------------------------------------
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const bf16x8 pf = pack_p(sacc[kb], 8 * c);
-        const char* vslice = vt + (kb * 32 + 16 * c) * Ly::kRowBytes;
-#pragma unroll
-        for (int db = 0; db < Ly::kDBlocks; ++db) {
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vslice + v_off[db]));
-          const s16x4 hi =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vslice + 8 * Ly::kRowBytes + v_off[db]));
-          const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pf, oacc[db], 0, 0, 0);
-        }
-      }
+  if (group == 1) next_phase();  // group 1 starts one phase late
+  for (int v = 0; v <= ntiles; v += kStages) {
+    iteration(std::integral_constant<int, 0>{}, v);
+    if (v + 1 > ntiles) break;
+    iteration(std::integral_constant<int, 1>{}, v + 1);
+    if (v + 2 > ntiles) break;
+    iteration(std::integral_constant<int, 2>{}, v + 2);
   }
+  if (group == 0) next_phase();  // group 0 ends one phase early
 
   // ---- write back ---------------------------------------------------------------
   const float l_tot = sum_with_partner(l_run);
