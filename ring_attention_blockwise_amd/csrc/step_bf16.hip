@@ -16,8 +16,8 @@
 //    VALU of each SIMD work at the same time ("ping-pong").
 //  * Keys are consumed in tiles of 64. K and V tiles are copied HBM -> LDS by
 //    16-byte buffer-to-LDS loads (bounds-checked by the buffer resource: rows
-//    past the block read as zero and are masked), in a ring of three LDS
-//    stages: a tile is loaded two phases before its first use.
+//    past the block read as zero and are masked), in a ring of four LDS
+//    stages: a tile is requested four phases before its first use.
 //  * The 16-byte units of each LDS row are XOR-swizzled through the global
 //    offset, so the K reads (16 lanes x 16 B over 16 rows) and the V
 //    transposed reads (4 rows x 4 units per half-wave) are free of bank
@@ -54,7 +54,12 @@ constexpr int kWaves = 8;               // two groups of four; w and w+4 share a
 constexpr int kThreads = kWaves * 64;
 constexpr int kBM = kWaves * 32;        // query rows per workgroup
 constexpr int kBN = 64;                 // keys per tile
-constexpr int kStages = 3;              // LDS ring of K/V tiles
+#ifndef RA_STAGES
+#define RA_STAGES 4
+#endif
+constexpr int kStages = RA_STAGES;      // LDS ring of K/V tiles (3 or 4)
+constexpr int kPrefetch = kStages - 2;  // tiles fetched ahead of the one in use
+static_assert(kStages == 3 || kStages == 4, "3 or 4 stages");
 #ifndef RA_LOOKAHEAD
 #define RA_LOOKAHEAD 6
 #endif
@@ -68,7 +73,8 @@ struct Layout {
   static constexpr int kTileBytes = kBN * kRowBytes;             // one K (or V) tile
   static constexpr int kVBase = kStages * kTileBytes;           // K stages, then V stages
   static constexpr int kSmemBytes = 2 * kStages * kTileBytes;
-  static constexpr int kLoadsPerWave = kTileBytes / 1024 / kWaves;  // 1 KB per wave-wide load
+  static constexpr int kLoaders = 4;                             // waves that copy tiles (group 1)
+  static constexpr int kLoadsPerWave = kTileBytes / 1024 / kLoaders;  // 1 KB per wave-wide load
   static constexpr int kDChunks = D / 16;                        // K=16 steps of S^T
   static constexpr int kDBlocks = D / 32;                        // 32-row blocks of O^T
   static_assert(kLoadsPerWave >= 1, "tile too small for the wave count");
@@ -146,9 +152,10 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 // Copy the K and V tile of 64 rows starting at local key `start` into one LDS
 // stage. The buffer resources bound the reads to the rows the block has: rows
 // past kv_len read as zero (their scores are masked).
+// `loader` (0..3) picks this wave's quarter of the tile.
 template <int D>
 __device__ __forceinline__ void issue_tile(const char* kg, const char* vg, int64_t kv_len, int32_t start,
-                                           uint32_t k_dst, uint32_t v_dst, int wave, int lane) {
+                                           uint32_t k_dst, uint32_t v_dst, int loader, int lane) {
   using Ly = Layout<D>;
   const int64_t left = kv_len - start;
   const int nbytes = (int)((left < kBN ? left : kBN) * Ly::kRowBytes);
@@ -157,10 +164,10 @@ __device__ __forceinline__ void issue_tile(const char* kg, const char* vg, int64
 #pragma unroll
   for (int i = 0; i < Ly::kLoadsPerWave; ++i) {
     // lane fills stored unit p of row r and fetches logical unit p ^ swz(r)
-    const int u = (wave * Ly::kLoadsPerWave + i) * 64 + lane;
+    const int u = (loader * Ly::kLoadsPerWave + i) * 64 + lane;
     const int r = u / Ly::kUnits;
     const int p = u % Ly::kUnits;
-    const uint32_t blk = (uint32_t)((wave * Ly::kLoadsPerWave + i) * 1024);
+    const uint32_t blk = (uint32_t)((loader * Ly::kLoadsPerWave + i) * 1024);
     dma16(rk, k_dst + blk, r * Ly::kRowBytes + ((p ^ Ly::k_swz(r)) << 4));
     dma16(rv, v_dst + blk, r * Ly::kRowBytes + ((p ^ Ly::v_swz(r)) << 4));
   }
@@ -173,6 +180,7 @@ constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 template <int N, int R, int AHEAD>
 __device__ __forceinline__ void pipeline_lds_mfma() {
+  if constexpr (AHEAD <= 0) return;  // leave the order to the compiler
   constexpr int kAhead = AHEAD < N ? AHEAD : N - 1;
   __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kAhead * R, 0);
 #pragma unroll
@@ -181,6 +189,52 @@ __device__ __forceinline__ void pipeline_lds_mfma() {
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, R, 0);
   }
   __builtin_amdgcn_sched_group_barrier(kSchedMfma, kAhead, 0);
+}
+
+// MFMA i of O^T += V^T P^T for the tile in stage ST: key block kb, 16-key
+// chunk c and head_dim block db, with V^T fetched by two transposing reads.
+template <int D, int ST>
+__device__ __forceinline__ void pv_mfma(int i, const uint32_t* v_addr, const bf16x8 (&pf)[2][2],
+                                        f32x16* oacc) {
+  using Ly = Layout<D>;
+  const int db = i % Ly::kDBlocks;
+  const int kc = i / Ly::kDBlocks;  // (kb, c) = (kc / 2, kc % 2)
+  const int slice = ST * Ly::kTileBytes + (kc * 16) * Ly::kRowBytes;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lds_ptr<s16x4>(v_addr[db] + slice));
+  const s16x4 hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lds_ptr<s16x4>(v_addr[db] + slice + 8 * Ly::kRowBytes));
+  const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pf[kc / 2][kc % 2], oacc[db],
+                                                     0, 0, 0);
+}
+
+// MFMA i of S^T = K Q^T for the tile in stage ST: key block kb = i % 2,
+// head_dim chunk c = i / 2.
+template <int D, int ST>
+__device__ __forceinline__ void s_mfma(int i, const uint32_t* k_addr, const bf16x8* qf, f32x16 (&sacc)[2]) {
+  using Ly = Layout<D>;
+  const int kb = i % 2;
+  const int c = i / 2;
+  const bf16x8 kf = *lds_ptr<bf16x8>(k_addr[c] + ST * Ly::kTileBytes + kb * 32 * Ly::kRowBytes);
+  sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sacc[kb], 0, 0, 0);
+}
+
+// Scheduling shape of NP P-V MFMAs (two LDS reads each) interleaved with NS
+// S MFMAs (one read each): operands are read two pairs ahead.
+template <int NP, int NS>
+__device__ __forceinline__ void pipeline_pv_s() {
+  static_assert(NS <= NP, "more S than P-V MFMAs");
+  constexpr int kAhead = 2;
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 3 * kAhead, 0);
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if (i + kAhead < NP) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    if (i < NS) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      if (i + kAhead < NS) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+  }
 }
 
 template <int D>
@@ -229,7 +283,18 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
   };
 
   const uint32_t smem_base = lds_address(smem);
-  if (ntiles > 0) issue_tile<D>(kg, vg, a.kv_len, tile_start(0), smem_base, smem_base + Ly::kVBase, wave, lane);
+  // Only group 1 copies tiles: it runs the softmax while group 0 runs the
+  // matrix phase, and issues the copies after its softmax, where it would
+  // otherwise wait at the barrier; the matrix waves never stall on loads.
+  auto issue = [&](int t) {
+    const uint32_t st = (uint32_t)(t % kStages) * Ly::kTileBytes;
+    issue_tile<D>(kg, vg, a.kv_len, tile_start(t), smem_base + st, smem_base + Ly::kVBase + st, wave - 4, lane);
+  };
+  if (group == 1) {
+#pragma unroll
+    for (int t = 0; t < kPrefetch; ++t)
+      if (t < ntiles) issue(t);
+  }
 
   // ---- Q^T fragments (B operand of S^T = K Q^T) ------------------------------
   bf16x8 qf[Ly::kDChunks];
@@ -311,20 +376,26 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
   // M_v = (P V of tile v-1, S of tile v) on the matrix cores and S_t the
   // softmax of tile t. Group 0 runs item i in phase i, group 1 in phase i+1;
   // every phase ends at a workgroup barrier, so all waves pass 2n+2 barriers.
-  // At the start of even phase 2u tile u has landed (it was issued in phase
-  // 2u-2) and tile u+1 is issued into the stage tile u-2 used, whose last
-  // reader finished in phase 2u-1. Tile t lives in stage t % 3; the tile loop
-  // is unrolled by three so that stage is a compile-time constant.
+  // The tile loop is unrolled by kStages so the stage is a compile-time
+  // constant.
   int ph = 0;
+  // Tile t lands in stage t % kStages. Group 1 issues tile t + kPrefetch + 1
+  // right after its softmax of tile t, in even phase 2(t+1) (tiles 0..kPrefetch
+  // before the loop and in its idle phase 0); that stage last held tile
+  // t + kPrefetch + 1 - kStages <= t - 1, read for the last time in phase 2t+1.
+  // At the start of even phase 2u the loading waves wait until tile u has
+  // landed (with four stages the copies of tile u+1 may still be in flight,
+  // issued after those of tile u; loads complete in order) and the
+  // barrier publishes it to every wave.
   auto next_phase = [&]() {
     const int u = ph >> 1;
-    const bool even = (ph & 1) == 0;
-    if (even && u < ntiles) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (even && u + 1 < ntiles) {
-      const uint32_t st = (uint32_t)((u + 1) % kStages) * Ly::kTileBytes;
-      issue_tile<D>(kg, vg, a.kv_len, tile_start(u + 1), smem_base + st, smem_base + Ly::kVBase + st, wave, lane);
+    if (group == 1 && (ph & 1) == 0 && u < ntiles) {
+      if (kPrefetch == 2 && u + 1 < ntiles)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * Layout<D>::kLoadsPerWave) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
+    __syncthreads();
     ++ph;
   };
 
@@ -334,40 +405,30 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
     constexpr int ST = decltype(st_tag)::value;
     constexpr int ST_PREV = (ST + kStages - 1) % kStages;
     next_phase();
-    if (v >= 1) {
-      // ---- O^T += V^T P^T for tile v-1 --------------------------------------
+    // ---- M_v: O^T += V^T P^T (tile v-1) interleaved with S^T = K Q^T (tile v).
+    // The two products use different accumulators, so alternating them keeps
+    // six independent MFMA chains in flight.
+    // v == 0 has no P-V yet (it is peeled off below); on the last iteration
+    // (v == ntiles) the S products read a stage holding an older tile and
+    // are never used, which keeps a single code path.
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+      for (int j = 0; j < 16; ++j) sacc[kb][j] = 0.0f;
+    if (v == 0) {
 #pragma unroll
-          for (int db = 0; db < Ly::kDBlocks; ++db) {
-            constexpr int base = ST_PREV * Ly::kTileBytes;
-            const int slice = base + (kb * 32 + 16 * c) * Ly::kRowBytes;
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)lds_ptr<s16x4>(v_addr[db] + slice));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)lds_ptr<s16x4>(v_addr[db] + slice + 8 * Ly::kRowBytes));
-            const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pf[kb][c],
-                                                               oacc[db], 0, 0, 0);
-          }
-        }
-      pipeline_lds_mfma<4 * Ly::kDBlocks, 2, kLookahead>();
-    }
-    if (v < ntiles) {
-      // ---- S^T = K Q^T for tile v, two 32-key blocks ----------------------------
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) sacc[kb][j] = 0.0f;
-#pragma unroll
-        for (int c = 0; c < Ly::kDChunks; ++c) {
-          const bf16x8 kf = *lds_ptr<bf16x8>(k_addr[c] + ST * Ly::kTileBytes + kb * 32 * Ly::kRowBytes);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sacc[kb], 0, 0, 0);
-        }
-      }
+      for (int i = 0; i < 2 * Ly::kDChunks; ++i) s_mfma<D, ST>(i, k_addr, qf, sacc);
       pipeline_lds_mfma<2 * Ly::kDChunks, 1, kLookahead>();
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4 * Ly::kDBlocks; ++i) {
+        pv_mfma<D, ST_PREV>(i, v_addr, pf, oacc);
+        if (i < 2 * Ly::kDChunks) s_mfma<D, ST>(i, k_addr, qf, sacc);
+      }
+      pipeline_pv_s<4 * Ly::kDBlocks, 2 * Ly::kDChunks>();
+    }
+    const bool do_s = v < ntiles;
+    if (do_s) {
       next_phase();
       // ---- softmax of tile v -------------------------------------------------------
       const bool first_range = v < plan.r0.ntiles;
@@ -415,16 +476,24 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int c = 0; c < 2; ++c) pf[kb][c] = pack_p(sacc[kb], 8 * c);
+      if (group == 1 && v + kPrefetch + 1 < ntiles) issue(v + kPrefetch + 1);
     }
   };
 
-  if (group == 1) next_phase();  // group 1 starts one phase late
+  if (group == 1) {  // group 1 starts one phase late
+    next_phase();
+    if (kPrefetch < ntiles) issue(kPrefetch);
+  }
   for (int v = 0; v <= ntiles; v += kStages) {
     iteration(std::integral_constant<int, 0>{}, v);
     if (v + 1 > ntiles) break;
     iteration(std::integral_constant<int, 1>{}, v + 1);
     if (v + 2 > ntiles) break;
     iteration(std::integral_constant<int, 2>{}, v + 2);
+    if constexpr (kStages == 4) {
+      if (v + 3 > ntiles) break;
+      iteration(std::integral_constant<int, 3 % kStages>{}, v + 3);
+    }
   }
   if (group == 0) next_phase();  // group 0 ends one phase early
 
