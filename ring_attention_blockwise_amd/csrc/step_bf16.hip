@@ -65,6 +65,7 @@ static_assert(kStages == 3 || kStages == 4, "3 or 4 stages");
 #endif
 constexpr int kLookahead = RA_LOOKAHEAD;  // MFMAs whose LDS operands are in flight
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer resource, dword access
+constexpr int kWaitVmcnt0 = 0x0F70;       // s_waitcnt vmcnt(0), other counters unchecked
 
 template <int D>
 struct Layout {
@@ -395,7 +396,11 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
       else
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    __syncthreads();
+    // Execution barrier only: a fence here would make every wave wait for
+    // all of its copies in flight, not just for the tile being published.
+    // LDS reads of the phase are complete (their data fed the MFMAs), and
+    // tile u was waited for above.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     ++ph;
   };
 
@@ -479,6 +484,12 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
       if (group == 1 && v + kPrefetch + 1 < ntiles) issue(v + kPrefetch + 1);
     }
   };
+
+  // Everything loaded so far (Q, the incoming state, the first tiles) must
+  // be in registers / LDS before the loop. The builtin (not asm) form lets
+  // the compiler see it, so it inserts no load waits inside the loop, where
+  // the hardware counter also counts the tile copies in flight.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   if (group == 1) {  // group 1 starts one phase late
     next_phase();
