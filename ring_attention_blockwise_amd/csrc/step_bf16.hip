@@ -59,7 +59,7 @@ constexpr int kBN = 64;                 // keys per tile
 #endif
 constexpr int kStages = RA_STAGES;      // LDS ring of K/V tiles (3 or 4)
 constexpr int kPrefetch = kStages - 2;  // tiles fetched ahead of the one in use
-static_assert(kStages == 3 || kStages == 4, "3 or 4 stages");
+static_assert(kStages == 4, "the copy schedule below assumes four stages");
 #ifndef RA_LOOKAHEAD
 #define RA_LOOKAHEAD 6
 #endif
@@ -74,8 +74,7 @@ struct Layout {
   static constexpr int kTileBytes = kBN * kRowBytes;             // one K (or V) tile
   static constexpr int kVBase = kStages * kTileBytes;           // K stages, then V stages
   static constexpr int kSmemBytes = 2 * kStages * kTileBytes;
-  static constexpr int kLoaders = 4;                             // waves that copy tiles (group 1)
-  static constexpr int kLoadsPerWave = kTileBytes / 1024 / kLoaders;  // 1 KB per wave-wide load
+  static constexpr int kLoadsPerWave = kTileBytes / 1024 / kWaves;  // per tensor per half tile, 1 KB each
   static constexpr int kDChunks = D / 16;                        // K=16 steps of S^T
   static constexpr int kDBlocks = D / 32;                        // 32-row blocks of O^T
   static_assert(kLoadsPerWave >= 1, "tile too small for the wave count");
@@ -153,10 +152,11 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 // Copy the K and V tile of 64 rows starting at local key `start` into one LDS
 // stage. The buffer resources bound the reads to the rows the block has: rows
 // past kv_len read as zero (their scores are masked).
-// `loader` (0..3) picks this wave's quarter of the tile.
+// One half of a tile: `half` picks the first or second half of the tile's 1 KB
+// blocks, `slot` (0..3) this wave's quarter of that half.
 template <int D>
 __device__ __forceinline__ void issue_tile(const char* kg, const char* vg, int64_t kv_len, int32_t start,
-                                           uint32_t k_dst, uint32_t v_dst, int loader, int lane) {
+                                           uint32_t k_dst, uint32_t v_dst, int half, int slot, int lane) {
   using Ly = Layout<D>;
   const int64_t left = kv_len - start;
   const int nbytes = (int)((left < kBN ? left : kBN) * Ly::kRowBytes);
@@ -165,10 +165,11 @@ __device__ __forceinline__ void issue_tile(const char* kg, const char* vg, int64
 #pragma unroll
   for (int i = 0; i < Ly::kLoadsPerWave; ++i) {
     // lane fills stored unit p of row r and fetches logical unit p ^ swz(r)
-    const int u = (loader * Ly::kLoadsPerWave + i) * 64 + lane;
+    const int b = half * (Ly::kTileBytes / 2048) + slot * Ly::kLoadsPerWave + i;  // 1 KB block of the tile
+    const int u = b * 64 + lane;
     const int r = u / Ly::kUnits;
     const int p = u % Ly::kUnits;
-    const uint32_t blk = (uint32_t)((loader * Ly::kLoadsPerWave + i) * 1024);
+    const uint32_t blk = (uint32_t)(b * 1024);
     dma16(rk, k_dst + blk, r * Ly::kRowBytes + ((p ^ Ly::k_swz(r)) << 4));
     dma16(rv, v_dst + blk, r * Ly::kRowBytes + ((p ^ Ly::v_swz(r)) << 4));
   }
@@ -284,18 +285,17 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
   };
 
   const uint32_t smem_base = lds_address(smem);
-  // Only group 1 copies tiles: it runs the softmax while group 0 runs the
-  // matrix phase, and issues the copies after its softmax, where it would
-  // otherwise wait at the barrier; the matrix waves never stall on loads.
+  // Tile copies are issued by the waves that run a softmax phase, right after
+  // their softmax, where they would otherwise wait at the barrier; the matrix
+  // waves never stall on load issue. Group g copies half g of each tile.
   auto issue = [&](int t) {
     const uint32_t st = (uint32_t)(t % kStages) * Ly::kTileBytes;
-    issue_tile<D>(kg, vg, a.kv_len, tile_start(t), smem_base + st, smem_base + Ly::kVBase + st, wave - 4, lane);
+    issue_tile<D>(kg, vg, a.kv_len, tile_start(t), smem_base + st, smem_base + Ly::kVBase + st, group, wave & 3,
+                  lane);
   };
-  if (group == 1) {
 #pragma unroll
-    for (int t = 0; t < kPrefetch; ++t)
-      if (t < ntiles) issue(t);
-  }
+  for (int t = 0; t < kPrefetch; ++t)
+    if (t < ntiles) issue(t);
 
   // ---- Q^T fragments (B operand of S^T = K Q^T) ------------------------------
   bf16x8 qf[Ly::kDChunks];
@@ -380,17 +380,16 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
   // The tile loop is unrolled by kStages so the stage is a compile-time
   // constant.
   int ph = 0;
-  // Tile t lands in stage t % kStages. Group 1 issues tile t + kPrefetch + 1
-  // right after its softmax of tile t, in even phase 2(t+1) (tiles 0..kPrefetch
-  // before the loop and in its idle phase 0); that stage last held tile
-  // t + kPrefetch + 1 - kStages <= t - 1, read for the last time in phase 2t+1.
-  // At the start of even phase 2u the loading waves wait until tile u has
-  // landed (with four stages the copies of tile u+1 may still be in flight,
-  // issued after those of tile u; loads complete in order) and the
-  // barrier publishes it to every wave.
+  // Tile t lands in stage t % kStages (four stages). Group 1 copies its half
+  // after its softmax of tile t-3 (phase 2t-4; its idle phase 0 for tile 2),
+  // group 0 after its softmax of tile t-2 (phase 2t-3); the stage last held
+  // tile t-4, read for the last time in phase 2t-5. At the start of even
+  // phase 2u each wave waits until its copies of tile u have landed (its
+  // copies of tile u+1 were issued after them and may still be in flight;
+  // loads complete in order) and the barrier publishes tile u.
   auto next_phase = [&]() {
     const int u = ph >> 1;
-    if (group == 1 && (ph & 1) == 0 && u < ntiles) {
+    if ((ph & 1) == 0 && u < ntiles) {
       if (kPrefetch == 2 && u + 1 < ntiles)
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * Layout<D>::kLoadsPerWave) : "memory");
       else
@@ -481,7 +480,10 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int c = 0; c < 2; ++c) pf[kb][c] = pack_p(sacc[kb], 8 * c);
-      if (group == 1 && v + kPrefetch + 1 < ntiles) issue(v + kPrefetch + 1);
+      {
+        const int t = v + (group == 1 ? 3 : 2);
+        if (t >= kPrefetch && t < ntiles) issue(t);
+      }
     }
   };
 
