@@ -64,6 +64,17 @@ static_assert(kStages == 4, "the copy schedule below assumes four stages");
 #define RA_LOOKAHEAD 6
 #endif
 constexpr int kLookahead = RA_LOOKAHEAD;  // MFMAs whose LDS operands are in flight
+#ifndef RA_PVS_AHEAD
+#define RA_PVS_AHEAD 4
+#endif
+constexpr int kPvsAhead = RA_PVS_AHEAD;  // same, for the interleaved P-V / S phase
+#ifndef RA_VPRE
+#define RA_VPRE 2
+#endif
+// P-V MFMAs of a matrix phase whose V^T operands are read at the end of the
+// wave's preceding softmax phase, before the barrier (the stage holding that
+// V tile was published two phases earlier and is not refilled until later).
+constexpr int kVPre = RA_VPRE;
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer resource, dword access
 constexpr int kWaitVmcnt0 = 0x0F70;       // s_waitcnt vmcnt(0), other counters unchecked
 
@@ -193,11 +204,11 @@ __device__ __forceinline__ void pipeline_lds_mfma() {
   __builtin_amdgcn_sched_group_barrier(kSchedMfma, kAhead, 0);
 }
 
-// MFMA i of O^T += V^T P^T for the tile in stage ST: key block kb, 16-key
-// chunk c and head_dim block db, with V^T fetched by two transposing reads.
+// Operand of MFMA i of O^T += V^T P^T for the tile in stage ST: key block
+// kb, 16-key chunk c and head_dim block db; V^T is fetched by two
+// transposing reads.
 template <int D, int ST>
-__device__ __forceinline__ void pv_mfma(int i, const uint32_t* v_addr, const bf16x8 (&pf)[2][2],
-                                        f32x16* oacc) {
+__device__ __forceinline__ bf16x8 read_vt(int i, const uint32_t* v_addr) {
   using Ly = Layout<D>;
   const int db = i % Ly::kDBlocks;
   const int kc = i / Ly::kDBlocks;  // (kb, c) = (kc / 2, kc % 2)
@@ -205,9 +216,15 @@ __device__ __forceinline__ void pv_mfma(int i, const uint32_t* v_addr, const bf1
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lds_ptr<s16x4>(v_addr[db] + slice));
   const s16x4 hi =
       __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lds_ptr<s16x4>(v_addr[db] + slice + 8 * Ly::kRowBytes));
-  const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pf[kc / 2][kc % 2], oacc[db],
-                                                     0, 0, 0);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <int D>
+__device__ __forceinline__ void pv_mfma(int i, const bf16x8& vt, const bf16x8 (&pf)[2][2], f32x16* oacc) {
+  using Ly = Layout<D>;
+  const int db = i % Ly::kDBlocks;
+  const int kc = i / Ly::kDBlocks;
+  oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, pf[kc / 2][kc % 2], oacc[db], 0, 0, 0);
 }
 
 // MFMA i of S^T = K Q^T for the tile in stage ST: key block kb = i % 2,
@@ -221,21 +238,33 @@ __device__ __forceinline__ void s_mfma(int i, const uint32_t* k_addr, const bf16
   sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sacc[kb], 0, 0, 0);
 }
 
-// Scheduling shape of NP P-V MFMAs (two LDS reads each) interleaved with NS
-// S MFMAs (one read each): operands are read two pairs ahead.
-template <int NP, int NS>
+// LDS reads taken by MFMA k of the interleaved order P-V 0, S 0, P-V 1,
+// S 1, ..., then the P-V MFMAs past NS: two per P-V MFMA (none for the first
+// PRE, whose operands were read earlier), one per S MFMA.
+constexpr int pvs_reads(int k, int NP, int NS, int PRE) {
+  if (k >= NP + NS) return 0;
+  if (k < 2 * NS) return (k & 1) ? 1 : ((k / 2) < PRE ? 0 : 2);
+  return (NS + k - 2 * NS) < PRE ? 0 : 2;
+}
+constexpr int pvs_reads_before(int n, int NP, int NS, int PRE) {
+  int r = 0;
+  for (int k = 0; k < n; ++k) r += pvs_reads(k, NP, NS, PRE);
+  return r;
+}
+
+// Scheduling shape of NP P-V MFMAs interleaved with NS S MFMAs: the operands
+// of MFMA k + AHEAD are read right after MFMA k is issued.
+template <int NP, int NS, int PRE, int AHEAD>
 __device__ __forceinline__ void pipeline_pv_s() {
   static_assert(NS <= NP, "more S than P-V MFMAs");
-  constexpr int kAhead = 2;
-  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 3 * kAhead, 0);
+  constexpr int kPro = pvs_reads_before(AHEAD, NP, NS, PRE);
+  if constexpr (kPro > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kPro, 0);
 #pragma unroll
-  for (int i = 0; i < NP; ++i) {
+  for (int k = 0; k < NP + NS; ++k) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    if (i + kAhead < NP) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-    if (i < NS) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      if (i + kAhead < NS) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    }
+    const int r = pvs_reads(k + AHEAD, NP, NS, PRE);
+    if (r == 1) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    if (r == 2) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
   }
 }
 
@@ -364,6 +393,7 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
 
   f32x16 sacc[2];
   bf16x8 pf[2][2];
+  bf16x8 vpre[kVPre > 0 ? kVPre : 1];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -397,9 +427,11 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
     }
     // Execution barrier only: a fence here would make every wave wait for
     // all of its copies in flight, not just for the tile being published.
-    // LDS reads of the phase are complete (their data fed the MFMAs), and
-    // tile u was waited for above.
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // Every LDS read of a matrix phase feeds an MFMA of that phase, so it has
+    // completed; reads issued at the end of a softmax phase (V^T operands of
+    // a tile published earlier) may still be in flight and are waited for
+    // at their first use.
+    asm volatile("s_barrier" ::: "memory");
     ++ph;
   };
 
@@ -426,10 +458,13 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
     } else {
 #pragma unroll
       for (int i = 0; i < 4 * Ly::kDBlocks; ++i) {
-        pv_mfma<D, ST_PREV>(i, v_addr, pf, oacc);
+        if (i < kVPre)
+          pv_mfma<D>(i, vpre[i < kVPre ? i : 0], pf, oacc);
+        else
+          pv_mfma<D>(i, read_vt<D, ST_PREV>(i, v_addr), pf, oacc);
         if (i < 2 * Ly::kDChunks) s_mfma<D, ST>(i, k_addr, qf, sacc);
       }
-      pipeline_pv_s<4 * Ly::kDBlocks, 2 * Ly::kDChunks>();
+      pipeline_pv_s<4 * Ly::kDBlocks, 2 * Ly::kDChunks, kVPre, kPvsAhead>();
     }
     const bool do_s = v < ntiles;
     if (do_s) {
@@ -484,6 +519,8 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
         const int t = v + (group == 1 ? 3 : 2);
         if (t >= kPrefetch && t < ntiles) issue(t);
       }
+#pragma unroll
+      for (int i = 0; i < kVPre; ++i) vpre[i] = read_vt<D, ST>(i, v_addr);
     }
   };
 
