@@ -88,6 +88,11 @@ def cpu_baseline(wl, rank, budget_s=12.0):
     }
 
 
+# Sources the bf16 step kernel is built from; a counter summary is only used
+# while their digest matches the one recorded with it.
+KERNEL_SOURCES = ("step_bf16.hip", "bf16_tiles.h", "common.h")
+
+
 def traffic_from_profile(kernel_name, workload_name):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source; else None."""
@@ -97,9 +102,11 @@ def traffic_from_profile(kernel_name, workload_name):
         return None
     with open(path) as f:
         rec = json.load(f)
-    src = os.path.join(ROOT, "ring_attention_blockwise_amd", "csrc", "step_bf16.hip")
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if rec.get("source_sha256") != digest:
+    digest = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "ring_attention_blockwise_amd", "csrc", name), "rb") as f:
+            digest.update(f.read())
+    if rec.get("source_sha256") != digest.hexdigest():
         return None
     return rec.get("bytes_per_launch")
 

@@ -36,30 +36,21 @@
 //    by more than 8 in base-2 units); O and l are rescaled only then.
 #include <type_traits>
 
-#include "common.h"
+#include "bf16_tiles.h"
 
 namespace ra {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+using namespace bf16k;
 
 constexpr int kWaves = 8;               // two groups of four; w and w+4 share a SIMD
 constexpr int kThreads = kWaves * 64;
 constexpr int kBM = kWaves * 32;        // query rows per workgroup
-constexpr int kBN = 64;                 // keys per tile
-#ifndef RA_STAGES
-#define RA_STAGES 4
-#endif
-constexpr int kStages = RA_STAGES;      // LDS ring of K/V tiles (3 or 4)
 constexpr int kPrefetch = kStages - 2;  // tiles fetched ahead of the one in use
 static_assert(kStages == 4, "the copy schedule below assumes four stages");
+// 1 KB copies per wave, per tensor and half tile
+template <int D>
+constexpr int kLoadsPerWave = Layout<D>::kTileBytes / 1024 / kWaves;
 #ifndef RA_LOOKAHEAD
 #define RA_LOOKAHEAD 6
 #endif
@@ -75,90 +66,6 @@ constexpr int kPvsAhead = RA_PVS_AHEAD;  // same, for the interleaved P-V / S ph
 // wave's preceding softmax phase, before the barrier (the stage holding that
 // V tile was published two phases earlier and is not refilled until later).
 constexpr int kVPre = RA_VPRE;
-constexpr int kBufferWord3 = 0x00020000;  // raw buffer resource, dword access
-constexpr int kWaitVmcnt0 = 0x0F70;       // s_waitcnt vmcnt(0), other counters unchecked
-
-template <int D>
-struct Layout {
-  static constexpr int kRowBytes = D * 2;                        // one K or V row
-  static constexpr int kUnits = D / 8;                           // 16-byte units per row
-  static constexpr int kTileBytes = kBN * kRowBytes;             // one K (or V) tile
-  static constexpr int kVBase = kStages * kTileBytes;           // K stages, then V stages
-  static constexpr int kSmemBytes = 2 * kStages * kTileBytes;
-  static constexpr int kLoadsPerWave = kTileBytes / 1024 / kWaves;  // per tensor per half tile, 1 KB each
-  static constexpr int kDChunks = D / 16;                        // K=16 steps of S^T
-  static constexpr int kDBlocks = D / 32;                        // 32-row blocks of O^T
-  static_assert(kLoadsPerWave >= 1, "tile too small for the wave count");
-
-  // Stored position of logical 16-byte unit c of row `row` is c ^ swz(row).
-  __device__ static __forceinline__ int k_swz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
-  __device__ static __forceinline__ int v_swz(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
-};
-
-__device__ __forceinline__ float max_with_partner(float x) {
-  // v_permlane32_swap(x, x): lanes < 32 get (x[l], x[l+32]), lanes >= 32
-  // get (x[l-32], x[l]); either way the pair max is max of the two.
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
-  return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
-}
-
-__device__ __forceinline__ float sum_with_partner(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
-  return __int_as_float(r[0]) + __int_as_float(r[1]);
-}
-
-__device__ __forceinline__ bf16x8 pack_p(const f32x16& s, int base) {
-  f32x2 a = {s[base + 0], s[base + 1]};
-  f32x2 b = {s[base + 2], s[base + 3]};
-  f32x2 c = {s[base + 4], s[base + 5]};
-  f32x2 d = {s[base + 6], s[base + 7]};
-  const bf16x2 pa = __builtin_convertvector(a, bf16x2);
-  const bf16x2 pb = __builtin_convertvector(b, bf16x2);
-  const bf16x2 pc = __builtin_convertvector(c, bf16x2);
-  const bf16x2 pd = __builtin_convertvector(d, bf16x2);
-  const auto ab = __builtin_shufflevector(pa, pb, 0, 1, 2, 3);
-  const auto cd = __builtin_shufflevector(pc, pd, 0, 1, 2, 3);
-  return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Raw buffer resource over `nbytes` bytes at `base` (wave-uniform).
-__device__ __forceinline__ i32x4 buffer_resource(const void* base, int nbytes) {
-  const uint64_t p = reinterpret_cast<uint64_t>(base);
-  i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
-  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));  // stride 0
-  r[2] = __builtin_amdgcn_readfirstlane(nbytes);
-  r[3] = kBufferWord3;
-  return r;
-}
-
-template <class T>
-__device__ __forceinline__ const __attribute__((address_space(3))) T* lds_ptr(uint32_t addr) {
-  return (const __attribute__((address_space(3))) T*)(uintptr_t)addr;
-}
-
-// One 16-byte-per-lane buffer load straight into LDS: lane i's 16 bytes land
-// at LDS byte address lds_base + 16*i. Issued through asm so the compiler
-// does not order later LDS reads of *other* stages behind it; the kernel
-// waits for it explicitly (vmcnt) before the barrier that publishes a tile.
-// M0 (the LDS destination) is saved and restored around the load.
-__device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t lds_base, int voff) {
-  int saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds_base), "v"(voff), "s"(rsrc)
-      : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_address(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
 
 // Copy the K and V tile of 64 rows starting at local key `start` into one LDS
 // stage. The buffer resources bound the reads to the rows the block has: rows
@@ -174,9 +81,9 @@ __device__ __forceinline__ void issue_tile(const char* kg, const char* vg, int64
   const i32x4 rk = buffer_resource(kg + (int64_t)start * Ly::kRowBytes, nbytes);
   const i32x4 rv = buffer_resource(vg + (int64_t)start * Ly::kRowBytes, nbytes);
 #pragma unroll
-  for (int i = 0; i < Ly::kLoadsPerWave; ++i) {
+  for (int i = 0; i < kLoadsPerWave<D>; ++i) {
     // lane fills stored unit p of row r and fetches logical unit p ^ swz(r)
-    const int b = half * (Ly::kTileBytes / 2048) + slot * Ly::kLoadsPerWave + i;  // 1 KB block of the tile
+    const int b = half * (Ly::kTileBytes / 2048) + slot * kLoadsPerWave<D> + i;  // 1 KB block of the tile
     const int u = b * 64 + lane;
     const int r = u / Ly::kUnits;
     const int p = u % Ly::kUnits;
@@ -189,8 +96,6 @@ __device__ __forceinline__ void issue_tile(const char* kg, const char* vg, int64
 // Scheduling shape of a block of N MFMAs that each take R LDS reads: the
 // reads run four MFMAs ahead of their use (enough to cover LDS latency)
 // instead of all being hoisted up front, which would exhaust the registers.
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedDsRead = 0x100;
 template <int N, int R, int AHEAD>
 __device__ __forceinline__ void pipeline_lds_mfma() {
   if constexpr (AHEAD <= 0) return;  // leave the order to the compiler
@@ -202,21 +107,6 @@ __device__ __forceinline__ void pipeline_lds_mfma() {
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, R, 0);
   }
   __builtin_amdgcn_sched_group_barrier(kSchedMfma, kAhead, 0);
-}
-
-// Operand of MFMA i of O^T += V^T P^T for the tile in stage ST: key block
-// kb, 16-key chunk c and head_dim block db; V^T is fetched by two
-// transposing reads.
-template <int D, int ST>
-__device__ __forceinline__ bf16x8 read_vt(int i, const uint32_t* v_addr) {
-  using Ly = Layout<D>;
-  const int db = i % Ly::kDBlocks;
-  const int kc = i / Ly::kDBlocks;  // (kb, c) = (kc / 2, kc % 2)
-  const int slice = ST * Ly::kTileBytes + (kc * 16) * Ly::kRowBytes;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lds_ptr<s16x4>(v_addr[db] + slice));
-  const s16x4 hi =
-      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lds_ptr<s16x4>(v_addr[db] + slice + 8 * Ly::kRowBytes));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 template <int D>
@@ -370,26 +260,12 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
   // compile-time offset (stage, key block, slice) that fits the 16-bit
   // offset field of the instruction.
   // K read (A operand of S^T): row kb*32 + qcol, logical unit 2c + hh.
-  const int k_swz = Ly::k_swz(qcol);
   uint32_t k_addr[Ly::kDChunks];
 #pragma unroll
-  for (int c = 0; c < Ly::kDChunks; ++c)
-    k_addr[c] = smem_base + qcol * Ly::kRowBytes + (((2 * c + hh) ^ k_swz) << 4);
-  // V^T read by ds_read_b64_tr_b16: within each 16-lane group, source lane
-  // s = 4t + q points at row (4*hh + t) of the 8-row slice and at head_dim
-  // offset 32*db + 16*(group16 & 1) + 4q; the instruction hands output lane j
-  // element j%4 of source lane 4t + j/4, i.e. V[row t][d = ... + j].
-  const int grp16 = lane >> 4;
-  const int t4 = (lane & 15) >> 2;
-  const int q4 = lane & 3;
-  const int v_row = 4 * hh + t4;
-  const int v_swz = Ly::v_swz(v_row);
+  for (int c = 0; c < Ly::kDChunks; ++c) k_addr[c] = k_read_address<D>(smem_base, qcol, hh, c);
   uint32_t v_addr[Ly::kDBlocks];
 #pragma unroll
-  for (int db = 0; db < Ly::kDBlocks; ++db) {
-    const int unit = 4 * db + 2 * (grp16 & 1) + (q4 >> 1);
-    v_addr[db] = smem_base + Ly::kVBase + v_row * Ly::kRowBytes + ((unit ^ v_swz) << 4) + ((q4 & 1) << 3);
-  }
+  for (int db = 0; db < Ly::kDBlocks; ++db) v_addr[db] = v_read_address<D>(smem_base, lane, db);
 
   f32x16 sacc[2];
   bf16x8 pf[2][2];
@@ -421,7 +297,7 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
     const int u = ph >> 1;
     if ((ph & 1) == 0 && u < ntiles) {
       if (kPrefetch == 2 && u + 1 < ntiles)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * Layout<D>::kLoadsPerWave) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kLoadsPerWave<D>) : "memory");
       else
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
