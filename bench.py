@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3         # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 DEFAULT_WORKLOAD = "zigzag128k_8dev_gqa"
 
 
@@ -109,6 +110,52 @@ def traffic_from_profile(kernel_name, workload_name):
     if rec.get("source_sha256") != digest.hexdigest():
         return None
     return rec.get("bytes_per_launch")
+
+
+def hbm_kernels(share, reps=20):
+    """GB/s of the HBM-bound pieces of the path at the share's shapes: the
+    state merge, the finalize pass and the D2D receive copy of one K block
+    (the copy ring_attn_forward issues). Bytes are the algorithmic ones: every
+    operand read once and every result written once."""
+    import torch
+    import ring_attention_blockwise_amd as ra
+    from ring_attention_blockwise_amd import harness
+
+    wl = share.workload
+    rd = share.ring_desc()
+    sd, _ = ra.ring_step_desc(rd, 0)
+    state_a = harness.run_steps(share, [0])
+    state_b = harness.run_steps(share, [1] if wl.world > 1 else [0])
+    out, lse = harness.alloc_outputs(share)
+    k0 = share.k_blocks[0]
+    recv = torch.empty_like(k0)
+    cur = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(cur)
+        for _ in range(reps):
+            fn()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    o_bytes = state_a[0].numel() * 4
+    ml_bytes = 2 * state_a[1].numel() * 4
+    out_bytes = out.numel() * out.element_size() + lse.numel() * 4
+    res = {}
+    for name, fn, nbytes in (
+        ("merge", lambda: ra.merge(sd, *state_a, *state_b), 3 * (o_bytes + ml_bytes)),
+        ("finalize", lambda: ra.finalize(sd, *state_a, out, lse), o_bytes + ml_bytes + out_bytes),
+        ("receive_copy", lambda: recv.copy_(k0), 2 * k0.numel() * k0.element_size()),
+    ):
+        ms = timed(fn)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"ms": round(ms, 4), "bytes": int(nbytes), "GB/s": round(gbs, 1),
+                     "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    return res
 
 
 def main():
@@ -192,6 +239,9 @@ def main():
     traffic = traffic_from_profile(kernel_name, wl.name)
     value = total_flops / (ms_per_step * 1e-3) / 1e12
 
+    hbm = hbm_kernels(share)
+    log(f"HBM-bound pieces: {hbm}")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
@@ -232,6 +282,7 @@ def main():
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
         },
+        "hbm_kernels": hbm,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
