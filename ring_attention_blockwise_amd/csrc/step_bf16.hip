@@ -9,11 +9,12 @@
 // Mapping (head_dim D in {64, 128}):
 //  * A workgroup of 8 waves owns 256 query rows of one (batch, q head); each
 //    wave owns 32 rows. Waves w and w+4 run on the same SIMD. The two groups
-//    (waves 0-3 and 4-7) are kept one phase apart by a workgroup barrier at
-//    every phase boundary: while one wave of a SIMD issues its matrix
-//    instructions (P V of tile t-1 and S of tile t), its partner runs the
-//    softmax of its own tile on the vector ALUs, so the MFMA pipe and the
-//    VALU of each SIMD work at the same time ("ping-pong").
+//    (waves 0-3 and 4-7) run one phase apart: in each tile interval group 0
+//    issues its matrix instructions (P V of tile t-1 and S of tile t) and
+//    then runs its softmax, group 1 the other way round, so while one wave of
+//    a SIMD keeps the MFMA pipe busy its partner works on the vector ALUs
+//    ("ping-pong"). The groups meet at a workgroup barrier once per tile,
+//    where the next tile is published.
 //  * Keys are consumed in tiles of 64. K and V tiles are copied HBM -> LDS by
 //    16-byte buffer-to-LDS loads (bounds-checked by the buffer resource: rows
 //    past the block read as zero and are masked), in a ring of four LDS
@@ -281,33 +282,41 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
 
   // Per wave the work is the sequence M_0 S_0 M_1 S_1 ... S_{n-1} M_n with
   // M_v = (P V of tile v-1, S of tile v) on the matrix cores and S_t the
-  // softmax of tile t. Group 0 runs item i in phase i, group 1 in phase i+1;
-  // every phase ends at a workgroup barrier, so all waves pass 2n+2 barriers.
-  // The tile loop is unrolled by kStages so the stage is a compile-time
-  // constant.
+  // softmax of tile t. Group 0 runs item i in phase i, group 1 in phase i+1.
+  // Only even phases start with a workgroup barrier (all waves pass n+1 of
+  // them); within the two phases between barriers each wave runs one matrix
+  // and one softmax phase at its own pace. The tile loop is unrolled by
+  // kStages so the stage is a compile-time constant.
   int ph = 0;
   // Tile t lands in stage t % kStages (four stages). Group 1 copies its half
   // after its softmax of tile t-3 (phase 2t-4; its idle phase 0 for tile 2),
   // group 0 after its softmax of tile t-2 (phase 2t-3); the stage last held
-  // tile t-4, read for the last time in phase 2t-5. At the start of even
+  // tile t-4, read for the last time in phase 2t-5, so the barrier that
+  // opens phase 2t-4 lies between its last read and the copies. At the start of even
   // phase 2u each wave waits until its copies of tile u have landed (its
   // copies of tile u+1 were issued after them and may still be in flight;
   // loads complete in order) and the barrier publishes tile u.
   auto next_phase = [&]() {
     const int u = ph >> 1;
-    if ((ph & 1) == 0 && u < ntiles) {
-      if (kPrefetch == 2 && u + 1 < ntiles)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kLoadsPerWave<D>) : "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if ((ph & 1) == 0) {
+      if (u < ntiles) {
+        if (kPrefetch == 2 && u + 1 < ntiles)
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kLoadsPerWave<D>) : "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      // Execution barrier only: a fence here would make every wave wait for
+      // all of its copies in flight, not just for the tile being published.
+      // Every LDS read of a matrix phase feeds an MFMA of that phase, so it
+      // has completed; reads issued at the end of a softmax phase (V^T
+      // operands of a tile published earlier) may still be in flight and are
+      // waited for at their first use.
+      asm volatile("s_barrier" ::: "memory");
     }
-    // Execution barrier only: a fence here would make every wave wait for
-    // all of its copies in flight, not just for the tile being published.
-    // Every LDS read of a matrix phase feeds an MFMA of that phase, so it has
-    // completed; reads issued at the end of a softmax phase (V^T operands of
-    // a tile published earlier) may still be in flight and are waited for
-    // at their first use.
-    asm volatile("s_barrier" ::: "memory");
+    // Odd phase boundaries need no barrier: nothing is published there, and
+    // every stage is refilled (after S_v: tile v+2 by group 0, tile v+3 by
+    // group 1) at least one even barrier after the last read of the tile it
+    // held.
     ++ph;
   };
 
