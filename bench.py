@@ -239,6 +239,24 @@ def main():
     traffic = traffic_from_profile(kernel_name, wl.name)
     value = total_flops / (ms_per_step * 1e-3) / 1e12
 
+    # The same forward captured once into a HIP graph and replayed: identical
+    # work (every step kernel and receive copy), without per-launch host cost.
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        harness.run_forward(share, copy_stream=copy_stream, workspace=ws, out=out, lse=lse)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(cur)
+    for _ in range(K):
+        graph.replay()
+    g1.record(cur)
+    torch.cuda.synchronize()
+    graph_ms = g0.elapsed_time(g1) / K
+    del graph
+    log(f"graph replay: {graph_ms:.3f} ms per forward")
+
     hbm = hbm_kernels(share)
     log(f"HBM-bound pieces: {hbm}")
 
@@ -282,6 +300,8 @@ def main():
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
         },
+        "graph_forward": {"ms_per_forward": round(graph_ms, 4),
+                          "value": round(total_flops / (graph_ms * 1e-3) / 1e12, 3)},
         "hbm_kernels": hbm,
         "cpu_baseline": cpu,
     }

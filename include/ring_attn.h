@@ -167,7 +167,12 @@ size_t ring_attn_forward_workspace_size(const ra_ring_desc* desc);
  *                  when step s has no visible key and launches nothing).
  * Steps whose block has no key visible to any local row launch no kernel;
  * the block is still received. Step kernels never read a slot while it is
- * being filled. */
+ * being filled. The two streams are ordered by four untimed hipEvent_t that
+ * the library creates on first use per calling thread and device and keeps
+ * until the thread ends (no other state survives a call). The copy stream
+ * forks from and joins back into compute_stream through these events, so a
+ * call can be captured into a HIP graph on compute_stream (pass
+ * step_events = NULL while capturing). */
 int ring_attn_forward(const ra_ring_desc* desc, const void* q_local,
                       const void* const* k_blocks, const void* const* v_blocks,
                       void* out, float* lse, void* workspace, size_t workspace_bytes,

@@ -345,24 +345,30 @@ size_t ring_attn_forward_workspace_size(const ra_ring_desc* d) {
 namespace {
 
 // Per-thread cache of the driver's synchronisation events (never timed).
+// The forward driver's ordering events: one untimed set per calling thread
+// and device, created on first use and kept for the life of the thread. A
+// thread enqueues one forward completely before the next, and a stream wait
+// binds to the record made just before it, so reusing the set is safe.
 struct DriverEvents {
-  int device = -1;
+  bool created = false;
   hipEvent_t ready[2] = {nullptr, nullptr};  // slot filled (copy stream)
   hipEvent_t freed[2] = {nullptr, nullptr};  // slot no longer read (compute stream)
 };
-thread_local DriverEvents g_events;
+constexpr int kMaxDevices = 64;
+thread_local DriverEvents g_events[kMaxDevices];
 
 hipError_t driver_events(DriverEvents** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  DriverEvents& ev = g_events;
-  if (ev.device != dev) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  DriverEvents& ev = g_events[dev];
+  if (!ev.created) {
     for (int i = 0; i < 2; ++i) {
       if ((e = hipEventCreateWithFlags(&ev.ready[i], hipEventDisableTiming)) != hipSuccess) return e;
       if ((e = hipEventCreateWithFlags(&ev.freed[i], hipEventDisableTiming)) != hipSuccess) return e;
     }
-    ev.device = dev;
+    ev.created = true;
   }
   *out = &ev;
   return hipSuccess;
@@ -428,8 +434,10 @@ int ring_attn_forward(const ra_ring_desc* d, const void* q_local, const void* co
   bool freed_recorded[2] = {false, false};
 
   // The copy stream must not start before work already queued on the compute
-  // stream that produced the inputs: order it after the compute stream once.
-  if (xs != cs) {
+  // stream that produced the inputs: order it after the compute stream once
+  // (only when something will be copied, so that a captured call leaves no
+  // branch of the copy stream unjoined).
+  if (xs != cs && n > 1) {
     if ((e = hipEventRecord(ev->freed[0], cs)) != hipSuccess) return hip_fail(e, "event record");
     if ((e = hipStreamWaitEvent(xs, ev->freed[0], 0)) != hipSuccess) return hip_fail(e, "stream wait");
   }
