@@ -158,6 +158,80 @@ def hbm_kernels(share, reps=20):
     return res
 
 
+def bench_ulysses(wl, rank, K, Wm):
+    """One device's Ulysses share: the whole call (gather, attention, scatter)
+    and, separately, its local attention on already head-sharded tensors;
+    the difference is the time of the two simulated all-to-alls."""
+    import torch
+    import ring_attention_blockwise_amd as ra
+    from ring_attention_blockwise_amd import harness
+
+    dev = torch.device("cuda:0")
+    P = wl.world
+    hr, hkr = wl.heads_q // P, wl.heads_kv // P
+    heads_q = list(range(rank * hr, (rank + 1) * hr))
+    heads_kv = list(range(rank * hkr, (rank + 1) * hkr))
+    q, k, v = harness.build_ulysses_shards(wl, dev, heads_q=heads_q, heads_kv=heads_kv)
+    dt = harness.torch_dtype(wl)
+    dtype = ra.BF16 if wl.dtype == "bf16" else ra.F32
+    L, B, d = wl.total_len, wl.batch, wl.head_dim
+    outs = [torch.empty((B, wl.heads_q, wl.local_len, d), dtype=dt, device=dev) for _ in range(P)]
+    lses = [torch.empty((B, wl.heads_q, wl.local_len), dtype=torch.float32, device=dev) for _ in range(P)]
+    ud = ra.ulysses_desc(B, wl.heads_q, wl.heads_kv, d, L, P, rank, dtype=dtype, causal=wl.causal)
+    ws = torch.empty(ra.ulysses_workspace_size(ud), dtype=torch.uint8, device=dev)
+    # the same attention on already head-sharded tensors: a one-device ring is
+    # exactly the single fused init+finalize launch the Ulysses call makes
+    qf = torch.cat([x[:, heads_q] for x in q], dim=2).contiguous()
+    kf = torch.cat([x[:, heads_kv] for x in k], dim=2).contiguous()
+    vf = torch.cat([x[:, heads_kv] for x in v], dim=2).contiguous()
+    rd = ra.ring_desc(B, hr, hkr, d, L, 1, 0, partition="contiguous", dtype=dtype, causal=wl.causal)
+    ws_r = torch.empty(ra.forward_workspace_size(rd), dtype=torch.uint8, device=dev)
+    out_f = torch.empty((B, hr, L, d), dtype=dt, device=dev)
+    lse_f = torch.empty((B, hr, L), dtype=torch.float32, device=dev)
+    cur = torch.cuda.current_stream()
+
+    def whole():
+        ra.ulysses_forward(ud, q, k, v, outs, lses, ws)
+
+    def attention():
+        ra.forward(rd, qf, [kf], [vf], out_f, lse_f, ws_r)
+
+    def timed(fn):
+        for _ in range(Wm):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(cur)
+        for _ in range(K):
+            fn()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+
+    ms_whole = timed(whole)
+    ms_attn = timed(attention)
+    pairs = L * (L + 1) // 2 if wl.causal else L * L
+    flops = 4.0 * d * hr * B * pairs
+    es = 2 if wl.dtype == "bf16" else 4
+    a2a_bytes = 2 * (B * (hr + 2 * hkr) * L * d * es) + 2 * (B * hr * L * (d * es + 4))  # read + write
+    a2a_ms = max(ms_whole - ms_attn, 1e-6)
+    value = flops / (ms_whole * 1e-3) / 1e12
+    rec = {
+        "metric": "effective causal attention TFLOP/s of one device's Ulysses share at 1 GPU",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": Wm,
+        "ms_per_step": round(ms_whole, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic (seeded, bf16-rounded; this device's heads only)",
+        "config": {"workload": wl.name, "description": wl.description, "batch": B, "heads_q": wl.heads_q,
+                   "heads_kv": wl.heads_kv, "head_dim": d, "global_seq_len": L, "world": P, "rank": rank,
+                   "parallelism": "one device's share of simulated DeepSpeed-Ulysses (all-to-alls as D2D copies)"},
+        "attention": {"ms": round(ms_attn, 4), "tflops": round(flops / (ms_attn * 1e-3) / 1e12, 2),
+                      "frac_of_bf16_peak": round(flops / (ms_attn * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "all_to_all": {"ms": round(a2a_ms, 4), "bytes": int(a2a_bytes),
+                       "GB/s": round(a2a_bytes / (a2a_ms * 1e-3) / 1e9, 1)},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -183,6 +257,10 @@ def main():
         sys.exit(1)
     ra.lib()  # fail loudly if the HIP library is not built
 
+    if args.workload in ring_inputs.ULYSSES_WORKLOADS:
+        wl = ring_inputs.ULYSSES_WORKLOADS[args.workload]
+        bench_ulysses(wl, wl.ranks[0] if args.rank is None else args.rank, args.steps, args.warmup)
+        return
     wl = ring_inputs.WORKLOADS[args.workload]
     rank = wl.ranks[0] if args.rank is None else args.rank
     dev = torch.device("cuda:0")

@@ -178,6 +178,51 @@ int ring_attn_forward(const ra_ring_desc* desc, const void* q_local,
                       void* out, float* lse, void* workspace, size_t workspace_bytes,
                       void* compute_stream, void* copy_stream, void* const* step_events);
 
+/* ---- Ulysses: sequence <-> head all-to-all around local attention --------- */
+
+/* One device's share of DeepSpeed-Ulysses ([L30] section 3.3, and the
+ * interview answer comparing it with the ring): the input is sharded along
+ * the sequence over `world` devices; a first all-to-all gives every device
+ * the whole sequence for heads_q/world query heads and heads_kv/world KV
+ * heads, the device runs full attention on them, and a second all-to-all
+ * restores the sequence sharding. Both head counts must be divisible by world
+ * ([L30] 3.4: with 8 KV heads Ulysses cannot go past 8 devices). */
+typedef struct {
+  int32_t batch;
+  int32_t heads_q;
+  int32_t heads_kv;
+  int32_t head_dim;
+  int64_t seq_len;                /* L, the global sequence; divisible by world */
+  int32_t dtype;
+  int32_t causal;                 /* positions are the global token indices */
+  float   scale;                  /* <= 0 means 1/sqrt(head_dim) */
+  int32_t world;                  /* >= 1; divides heads_q, heads_kv and seq_len */
+  int32_t rank;                   /* this device, 0 <= rank < world */
+} ra_ulysses_desc;
+
+/* Bytes of workspace ring_attn_ulysses_forward needs: this device's
+ * head-sharded Q, K, V, output and LSE over the whole sequence. 0 on a bad
+ * desc. */
+size_t ring_attn_ulysses_workspace_size(const ra_ulysses_desc* desc);
+
+/* Device `rank`'s part of one Ulysses attention, simulated on one device:
+ * the other devices' shards sit in this device's memory and each all-to-all
+ * is this device's share of strided device-to-device copies.
+ *   q_shards[j], out_shards[j]   [B, Hq,  L/world, d] dtype: device j's rows
+ *                                j*L/world .. (j+1)*L/world - 1.
+ *   k_shards[j], v_shards[j]     [B, Hkv, L/world, d] dtype.
+ *   lse_shards[j]                [B, Hq,  L/world] fp32; the array may be NULL.
+ *   (HOST arrays of `world` DEVICE pointers.)
+ * Reads query heads rank*Hq/world .. (rank+1)*Hq/world - 1 (and the matching
+ * KV heads) of every shard and writes the same heads of every out (and lse)
+ * shard; running every rank fills the outputs. All work is enqueued on
+ * `stream`: gather (first all-to-all), one attention launch (init and
+ * finalize fused), scatter (second all-to-all). */
+int ring_attn_ulysses_forward(const ra_ulysses_desc* desc, const void* const* q_shards,
+                              const void* const* k_shards, const void* const* v_shards,
+                              void* const* out_shards, float* const* lse_shards,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- host-only helpers (no device work) ---------------------------------- */
 
 /* Segments of device `rank`'s local rows under `partition` (RA_PART_*).

@@ -29,7 +29,7 @@ EXPORTED = (
     "ring_attn_forward", "ring_attn_partition_segments", "ring_attn_ring_step_desc",
     "ring_attn_visible_pairs", "ring_attn_last_error", "ring_attn_abi_version",
     "ring_attn_events_create", "ring_attn_event_elapsed_ms", "ring_attn_events_destroy",
-    "ring_attn_synchronize",
+    "ring_attn_synchronize", "ring_attn_ulysses_workspace_size", "ring_attn_ulysses_forward",
 )
 
 
@@ -56,6 +56,15 @@ class RingDesc(ctypes.Structure):
     ]
 
 
+class UlyssesDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("seq_len", ctypes.c_int64), ("dtype", ctypes.c_int32),
+        ("causal", ctypes.c_int32), ("scale", ctypes.c_float), ("world", ctypes.c_int32),
+        ("rank", ctypes.c_int32),
+    ]
+
+
 class RingAttnError(RuntimeError):
     def __init__(self, code: int, message: str):
         super().__init__(f"[{code}] {message}")
@@ -74,7 +83,7 @@ def lib() -> ctypes.CDLL:
                 f"{LIB_PATH} is missing: build it with `python -m ring_attention_blockwise_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
         P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
-        SD, RD = ctypes.POINTER(StepDesc), ctypes.POINTER(RingDesc)
+        SD, RD, UD = ctypes.POINTER(StepDesc), ctypes.POINTER(RingDesc), ctypes.POINTER(UlyssesDesc)
         sig = {
             "ring_attn_step": (ctypes.c_int, [SD, P, P, P, P, P, P, I32, P]),
             "ring_attn_merge": (ctypes.c_int, [SD, P, P, P, P, P, P, P]),
@@ -91,6 +100,8 @@ def lib() -> ctypes.CDLL:
             "ring_attn_event_elapsed_ms": (ctypes.c_int, [P, P, ctypes.POINTER(ctypes.c_float)]),
             "ring_attn_events_destroy": (ctypes.c_int, [I32, P]),
             "ring_attn_synchronize": (ctypes.c_int, [P]),
+            "ring_attn_ulysses_workspace_size": (SZ, [UD]),
+            "ring_attn_ulysses_forward": (ctypes.c_int, [UD, P, P, P, P, P, P, SZ, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -260,6 +271,48 @@ def forward(rd: RingDesc, q_local, k_blocks: Sequence, v_blocks: Sequence, out, 
         _ptr(out, dt, (B, Hq, c, D), "out"), _ptr(lse, torch.float32, (B, Hq, c), "lse"),
         ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(compute_stream),
         None if copy_stream is None else ctypes.c_void_p(copy_stream.cuda_stream), ev), "ring_attn_forward")
+
+
+def ulysses_desc(batch, heads_q, heads_kv, head_dim, seq_len, world, rank, dtype=BF16, causal=True,
+                 scale=0.0) -> UlyssesDesc:
+    return UlyssesDesc(batch, heads_q, heads_kv, head_dim, seq_len, dtype, int(causal), scale, world, rank)
+
+
+def ulysses_workspace_size(ud: UlyssesDesc) -> int:
+    n = lib().ring_attn_ulysses_workspace_size(ctypes.byref(ud))
+    if n == 0:
+        raise RingAttnError(ERR_INVALID_ARG, f"ulysses_workspace_size: {last_error()}")
+    return int(n)
+
+
+def ulysses_forward(ud: UlyssesDesc, q_shards: Sequence, k_shards: Sequence, v_shards: Sequence,
+                    out_shards: Sequence, lse_shards: Optional[Sequence], workspace, stream=None):
+    """Device ``ud.rank``'s part of one Ulysses attention (ring_attn_ulysses_forward):
+    shards are device j's [B, H, L/world, d] tensors; writes this device's heads of
+    every out (and lse) shard. ``workspace`` is a uint8 GPU tensor."""
+    torch = _torch()
+    dt = _dtype_of(ud.dtype)
+    B, Hq, Hk, D, n = ud.batch, ud.heads_q, ud.heads_kv, ud.head_dim, ud.world
+    ls = ud.seq_len // n if n > 0 else 0
+    for name, arr in (("q", q_shards), ("k", k_shards), ("v", v_shards), ("out", out_shards)):
+        if len(arr) != n:
+            raise ValueError(f"need {n} {name} shards")
+    if lse_shards is not None and len(lse_shards) != n:
+        raise ValueError(f"need {n} lse shards")
+
+    def ptrs(arr, dtype, heads, name):
+        return (ctypes.c_void_p * n)(*[_ptr(t, dtype, (B, heads, ls, D), f"{name}[{i}]").value
+                                      for i, t in enumerate(arr)])
+
+    qp, kp, vp = ptrs(q_shards, dt, Hq, "q_shards"), ptrs(k_shards, dt, Hk, "k_shards"), ptrs(v_shards, dt, Hk, "v_shards")
+    op = ptrs(out_shards, dt, Hq, "out_shards")
+    lp = None
+    if lse_shards is not None:
+        lp = (ctypes.c_void_p * n)(*[_ptr(t, torch.float32, (B, Hq, ls), f"lse_shards[{i}]").value
+                                     for i, t in enumerate(lse_shards)])
+    ws = _ptr(workspace, torch.uint8, (workspace.numel(),), "workspace")
+    _check(lib().ring_attn_ulysses_forward(ctypes.byref(ud), qp, kp, vp, op, lp, ws, workspace.numel(),
+                                           _stream(stream)), "ring_attn_ulysses_forward")
 
 
 class StepEvents:

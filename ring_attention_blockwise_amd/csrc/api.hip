@@ -217,7 +217,7 @@ extern "C" {
 
 const char* ring_attn_last_error(void) { return g_last_error; }
 
-int32_t ring_attn_abi_version(void) { return 100; }
+int32_t ring_attn_abi_version(void) { return 101; }
 
 int ring_attn_partition_segments(int32_t partition, int32_t world, int32_t rank, int64_t local_len,
                                  ra_segment* segs, int32_t* n_segs) {
@@ -504,6 +504,172 @@ int ring_attn_forward(const ra_ring_desc* d, const void* q_local, const void* co
   }
   // The copy stream's last work is ordered before the compute stream's last
   // step (which waited on it), so the caller only needs to sync compute_stream.
+  return RA_OK;
+}
+
+namespace {
+
+struct UlyssesLayout {
+  int64_t hq, hkv, ls;  // heads of this device, rows per shard
+  size_t es;            // element size
+  size_t off_q, off_k, off_v, off_out, off_lse, total;
+};
+
+int check_ulysses_desc(const ra_ulysses_desc* d) {
+  if (d == nullptr) return fail(RA_ERR_INVALID_ARG, "ulysses desc is NULL");
+  if (d->world < 1) return fail(RA_ERR_INVALID_ARG, "world must be >= 1");
+  if (d->rank < 0 || d->rank >= d->world) return fail(RA_ERR_INVALID_ARG, "rank out of range");
+  if (d->causal != 0 && d->causal != 1) return fail(RA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (d->seq_len < 0 || d->seq_len > kMaxRows) return fail(RA_ERR_INVALID_ARG, "seq_len out of range");
+  if (d->heads_q < 1 || d->heads_kv < 1 || d->heads_q % d->world != 0 || d->heads_kv % d->world != 0)
+    return fail(RA_ERR_INVALID_ARG, "heads_q (%d) and heads_kv (%d) must be divisible by world (%d)", d->heads_q,
+                d->heads_kv, d->world);
+  if (d->seq_len % d->world != 0)
+    return fail(RA_ERR_INVALID_ARG, "seq_len (%lld) must be divisible by world (%d)", (long long)d->seq_len,
+                d->world);
+  // the attention this device runs: its heads over the whole sequence
+  ra_step_desc s{};
+  s.batch = d->batch;
+  s.heads_q = d->heads_q / d->world;
+  s.heads_kv = d->heads_kv / d->world;
+  s.head_dim = d->head_dim;
+  s.q_len = d->seq_len;
+  s.kv_len = d->seq_len;
+  s.dtype = d->dtype;
+  s.scale = d->scale;
+  return check_shape(&s, true);
+}
+
+void ulysses_layout(const ra_ulysses_desc* d, UlyssesLayout* L) {
+  L->hq = d->heads_q / d->world;
+  L->hkv = d->heads_kv / d->world;
+  L->ls = d->seq_len / d->world;
+  L->es = d->dtype == RA_BF16 ? 2 : 4;
+  const size_t rows_q = (size_t)d->batch * L->hq * (size_t)d->seq_len;
+  const size_t rows_kv = (size_t)d->batch * L->hkv * (size_t)d->seq_len;
+  size_t off = 0;
+  L->off_q = off;
+  off += align256(rows_q * d->head_dim * L->es);
+  L->off_k = off;
+  off += align256(rows_kv * d->head_dim * L->es);
+  L->off_v = off;
+  off += align256(rows_kv * d->head_dim * L->es);
+  L->off_out = off;
+  off += align256(rows_q * d->head_dim * L->es);
+  L->off_lse = off;
+  off += align256(rows_q * 4);
+  L->total = off + 256;  // room to align the caller's base pointer
+}
+
+// One all-to-all leg for this device, as strided copies: for every shard j
+// and batch b, `rows` consecutive heads of `width` bytes each move between
+// the shard (head pitch `shard_pitch`, first head `shard_head`, heads per
+// batch `shard_heads`) and the head-sharded buffer (head pitch `full_pitch`,
+// segment j at byte j * width). to_shards picks the direction.
+hipError_t all_to_all_leg(const ra_ulysses_desc* d, char* full, const char* const* shards_in,
+                          char* const* shards_out, int64_t rows, int64_t shard_heads, int64_t shard_head,
+                          size_t width, size_t full_pitch, hipStream_t s) {
+  for (int j = 0; j < d->world; ++j)
+    for (int b = 0; b < d->batch; ++b) {
+      char* fptr = full + ((size_t)b * rows) * full_pitch + (size_t)j * width;
+      const size_t shard_off = ((size_t)b * shard_heads + shard_head) * width;
+      hipError_t e;
+      if (shards_out)
+        e = hipMemcpy2DAsync(shards_out[j] + shard_off, width, fptr, full_pitch, width, rows,
+                             hipMemcpyDeviceToDevice, s);
+      else
+        e = hipMemcpy2DAsync(fptr, full_pitch, shards_in[j] + shard_off, width, width, rows,
+                             hipMemcpyDeviceToDevice, s);
+      if (e != hipSuccess) return e;
+    }
+  return hipSuccess;
+}
+
+}  // namespace
+
+size_t ring_attn_ulysses_workspace_size(const ra_ulysses_desc* d) {
+  if (check_ulysses_desc(d) != RA_OK) return 0;
+  UlyssesLayout L;
+  ulysses_layout(d, &L);
+  return L.total;
+}
+
+int ring_attn_ulysses_forward(const ra_ulysses_desc* d, const void* const* q_shards, const void* const* k_shards,
+                              const void* const* v_shards, void* const* out_shards, float* const* lse_shards,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_ulysses_desc(d);
+  if (rc) return rc;
+  if (!q_shards || !k_shards || !v_shards || !out_shards)
+    return fail(RA_ERR_INVALID_ARG, "q/k/v/out shard arrays must not be NULL");
+  const bool has_rows = d->seq_len > 0 && d->batch > 0;
+  if (has_rows)
+    for (int j = 0; j < d->world; ++j) {
+      if (!q_shards[j] || !k_shards[j] || !v_shards[j] || !out_shards[j])
+        return fail(RA_ERR_INVALID_ARG, "shard %d pointer is NULL", j);
+      if (!aligned16(q_shards[j]) || !aligned16(k_shards[j]) || !aligned16(v_shards[j]) || !aligned16(out_shards[j]))
+        return fail(RA_ERR_INVALID_ARG, "shard %d is not 16-byte aligned", j);
+      if (lse_shards && !lse_shards[j]) return fail(RA_ERR_INVALID_ARG, "lse shard %d pointer is NULL", j);
+    }
+  UlyssesLayout L;
+  ulysses_layout(d, &L);
+  if (workspace == nullptr || workspace_bytes < L.total)
+    return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, workspace_bytes);
+  if (!has_rows) return RA_OK;
+
+  char* base = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~(uintptr_t)255);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t row_bytes = (size_t)d->head_dim * L.es;
+  const size_t seg = (size_t)L.ls * row_bytes;         // one head of one shard
+  const size_t full = (size_t)d->seq_len * row_bytes;  // one head of the whole sequence
+  const char* const* qs = reinterpret_cast<const char* const*>(q_shards);
+  const char* const* ks = reinterpret_cast<const char* const*>(k_shards);
+  const char* const* vs = reinterpret_cast<const char* const*>(v_shards);
+  hipError_t e;
+  // first all-to-all: this device's heads of every sequence shard
+  if ((e = all_to_all_leg(d, base + L.off_q, qs, nullptr, L.hq, d->heads_q, (int64_t)d->rank * L.hq, seg, full,
+                          s)) != hipSuccess ||
+      (e = all_to_all_leg(d, base + L.off_k, ks, nullptr, L.hkv, d->heads_kv, (int64_t)d->rank * L.hkv, seg, full,
+                          s)) != hipSuccess ||
+      (e = all_to_all_leg(d, base + L.off_v, vs, nullptr, L.hkv, d->heads_kv, (int64_t)d->rank * L.hkv, seg, full,
+                          s)) != hipSuccess)
+    return hip_fail(e, "ulysses gather");
+
+  // local attention: every query of the sequence against every key, for this
+  // device's heads, in one launch with the state kept in registers
+  ra::StepArgs a{};
+  a.q_len = d->seq_len;
+  a.kv_len = d->seq_len;
+  a.batch = d->batch;
+  a.heads_q = (int32_t)L.hq;
+  a.heads_kv = (int32_t)L.hkv;
+  a.group = (int32_t)(L.hq / L.hkv);
+  const double scale = d->scale > 0.0f ? (double)d->scale : 1.0 / std::sqrt((double)d->head_dim);
+  a.scale_log2 = (float)(scale * 1.4426950408889634074);
+  a.causal = d->causal;
+  a.n_q_seg = 1;
+  a.n_kv_seg = 1;
+  a.qs[0] = {0, d->seq_len, 1};
+  a.ks[0] = {0, d->seq_len, 1};
+  a.q = base + L.off_q;
+  a.k = base + L.off_k;
+  a.v = base + L.off_v;
+  a.init = 1;
+  a.final_ = 1;
+  a.out = base + L.off_out;
+  a.lse = reinterpret_cast<float*>(base + L.off_lse);
+  if ((e = launch_step(a, d->head_dim, d->dtype, s)) != hipSuccess) return hip_fail(e, "ulysses attention launch");
+
+  // second all-to-all: this device's heads back into every sequence shard
+  char* const* os = reinterpret_cast<char* const*>(out_shards);
+  if ((e = all_to_all_leg(d, base + L.off_out, nullptr, os, L.hq, d->heads_q, (int64_t)d->rank * L.hq, seg, full,
+                          s)) != hipSuccess)
+    return hip_fail(e, "ulysses scatter");
+  if (lse_shards) {
+    char* const* ls = reinterpret_cast<char* const*>(lse_shards);
+    if ((e = all_to_all_leg(d, base + L.off_lse, nullptr, ls, L.hq, d->heads_q, (int64_t)d->rank * L.hq,
+                            (size_t)L.ls * 4, (size_t)d->seq_len * 4, s)) != hipSuccess)
+      return hip_fail(e, "ulysses scatter (lse)");
+  }
   return RA_OK;
 }
 

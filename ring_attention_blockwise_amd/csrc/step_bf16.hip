@@ -165,16 +165,34 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
   using Ly = Layout<D>;
   __shared__ __attribute__((aligned(1024))) char smem[Ly::kSmemBytes];
 
-  // ---- work item: XCD-major so one XCD streams one KV head -----------------
-  const int32_t item = (int32_t)(blockIdx.x % 8) * items_per_xcd + (int32_t)(blockIdx.x / 8);
-  if (item >= n_items) return;
-  const int32_t per_kv = q_tiles * a.group;
-  const int32_t bk = item / per_kv;
-  const int32_t rem = item % per_kv;
-  const int32_t tile = q_tiles - 1 - rem / a.group;  // heavy (late) tiles first
-  const int32_t kvh = bk % a.heads_kv;
-  const int32_t b = bk / a.heads_kv;
-  const int32_t h = kvh * a.group + rem % a.group;
+  // ---- work item ------------------------------------------------------------
+  // Workgroup i runs on XCD i % 8. When the (batch, KV head) pairs divide
+  // evenly over the 8 XCDs, each XCD takes whole KV heads (its L2 streams
+  // their K/V), heavy (late) causal tiles first. Otherwise (e.g. one KV head)
+  // that would hand the heavy tiles to some XCDs and the light ones to
+  // others, so the heavy-first order is dealt round-robin over all XCDs.
+  int32_t tile, b, h;
+  {
+    const int32_t n_bk = a.batch * a.heads_kv;
+    if (n_bk % 8 == 0) {
+      const int32_t item = (int32_t)(blockIdx.x % 8) * items_per_xcd + (int32_t)(blockIdx.x / 8);
+      if (item >= n_items) return;
+      const int32_t per_kv = q_tiles * a.group;
+      const int32_t bk = item / per_kv;
+      const int32_t rem = item % per_kv;
+      tile = q_tiles - 1 - rem / a.group;
+      b = bk / a.heads_kv;
+      h = (bk % a.heads_kv) * a.group + rem % a.group;
+    } else {
+      const int32_t item = (int32_t)blockIdx.x;
+      if (item >= n_items) return;
+      const int32_t n_bh = a.batch * a.heads_q;
+      tile = q_tiles - 1 - item / n_bh;
+      b = (item % n_bh) / a.heads_q;
+      h = (item % n_bh) % a.heads_q;
+    }
+  }
+  const int32_t kvh = h / a.group;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

@@ -96,6 +96,27 @@ def build_share(wl: ring_inputs.Workload, rank: int, device, on_head=None) -> De
     return DeviceShare(wl, rank, q, k_blocks, v_blocks, qpos)
 
 
+def build_ulysses_shards(wl: ring_inputs.Workload, device, heads_q=None, heads_kv=None):
+    """Every device's sequence shard of Q, K and V for a Ulysses workload:
+    lists of ``world`` tensors [B, H, local_len, d], shard j holding tokens
+    j*local_len .. (j+1)*local_len - 1 (only ``heads_q`` / ``heads_kv`` are
+    drawn if given; the others stay zero)."""
+    import torch
+    dt = torch_dtype(wl)
+    B, Hq, Hk, d, c, n = wl.batch, wl.heads_q, wl.heads_kv, wl.head_dim, wl.local_len, wl.world
+    out = {}
+    for name, H, which in (("q", Hq, heads_q), ("k", Hk, heads_kv), ("v", Hk, heads_kv)):
+        shards = [torch.zeros((B, H, c, d), dtype=dt, device=device) for _ in range(n)]
+        for b in range(B):
+            for h in (range(H) if which is None else which):
+                full = _to_device(ring_inputs.head(wl, name, b, h), dt, device)
+                for j in range(n):
+                    shards[j][b, h] = full[j * c:(j + 1) * c]
+                del full
+        out[name] = shards
+    return out["q"], out["k"], out["v"]
+
+
 def alloc_outputs(share: DeviceShare):
     import torch
     wl = share.workload

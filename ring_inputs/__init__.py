@@ -107,6 +107,26 @@ WORKLOADS = {
 }
 
 
+# Ulysses workloads: the global sequence is split into `world` contiguous
+# shards (device j holds tokens j*local_len .. (j+1)*local_len - 1); the
+# 128K one draws the same global tensors as the 128K zigzag ring workload.
+ULYSSES_WORKLOADS = {
+    "ulysses2k_4dev_gqa": Workload(
+        name="ulysses2k_4dev_gqa", batch=1, heads_q=8, heads_kv=4, head_dim=128, dtype="bf16",
+        causal=True, partition="contiguous", world=4, local_len=512, seed=1006, ranks=(0, 1, 2, 3),
+        description="Ulysses, causal, 2048 tokens over 4 devices, 8 Q / 4 KV heads, d128 bf16"),
+    "ulysses512_2dev_f32": Workload(
+        name="ulysses512_2dev_f32", batch=2, heads_q=4, heads_kv=2, head_dim=64, dtype="f32",
+        causal=False, partition="contiguous", world=2, local_len=256, seed=1007, ranks=(0, 1),
+        description="Ulysses, non-causal, 512 tokens over 2 devices, B2, 4 Q / 2 KV heads, d64 fp32"),
+    "ulysses128k_8dev_gqa": Workload(
+        name="ulysses128k_8dev_gqa", batch=1, heads_q=32, heads_kv=8, head_dim=128, dtype="bf16",
+        causal=True, partition="contiguous", world=8, local_len=16384, seed=1003, ranks=(0,),
+        description="Ulysses, one device of a 128K causal context over 8 devices, 32 Q / 8 KV heads "
+                    "(4 Q / 1 KV head per device), d128 bf16"),
+}
+
+
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even); float32 out."""
     x = np.ascontiguousarray(x, dtype=np.float32)

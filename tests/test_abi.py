@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert ra.lib().ring_attn_abi_version() == 100
+    assert ra.lib().ring_attn_abi_version() == 101
 
 
 def _expand(segs):
@@ -164,6 +164,35 @@ def test_forward_rejects_small_workspace_and_bad_desc():
     same = ctypes.c_void_p(0x5000)
     assert L.ring_attn_forward(ctypes.byref(rd), FAKE, blocks, blocks, FAKE, FAKE, FAKE, ws, same, same,
                                None) == ra.ERR_INVALID_ARG
+
+
+def test_ulysses_workspace_and_validation():
+    """Head counts and sequence length must divide by world; bad arguments are
+    rejected on the host before anything is enqueued."""
+    L = ra.lib()
+    ud = ra.ulysses_desc(1, 8, 4, 128, 2048, 4, 1)
+    ws = ra.ulysses_workspace_size(ud)
+    # this device: 2 Q heads and 1 KV head over all 2048 tokens (Q, K, V, out bf16, LSE fp32)
+    assert ws >= (2 + 1 + 1 + 2) * 2048 * 128 * 2 + 2 * 2048 * 4
+    for bad in (ra.ulysses_desc(1, 8, 4, 128, 2048, 8, 0),   # 4 KV heads over 8 devices
+                ra.ulysses_desc(1, 6, 3, 128, 2048, 4, 0),   # 6 Q heads over 4 devices
+                ra.ulysses_desc(1, 8, 4, 128, 2050, 4, 0),   # 2050 tokens over 4 devices
+                ra.ulysses_desc(1, 8, 4, 128, 2048, 4, 4),   # rank out of range
+                ra.ulysses_desc(1, 8, 4, 96, 2048, 4, 0)):   # head_dim not 64 or 128
+        assert L.ring_attn_ulysses_workspace_size(ctypes.byref(bad)) == 0
+    shards = (ctypes.c_void_p * 4)(*([0x10000] * 4))
+    rc = L.ring_attn_ulysses_forward(ctypes.byref(ud), shards, shards, shards, shards, None, FAKE, ws - 1, None)
+    assert rc == ra.ERR_WORKSPACE
+    nulls = (ctypes.c_void_p * 4)(*([0x10000] * 3 + [None]))
+    rc = L.ring_attn_ulysses_forward(ctypes.byref(ud), shards, nulls, shards, shards, None, FAKE, ws, None)
+    assert rc == ra.ERR_INVALID_ARG
+    misaligned = (ctypes.c_void_p * 4)(*([0x10000] * 3 + [0x10008]))
+    rc = L.ring_attn_ulysses_forward(ctypes.byref(ud), shards, shards, shards, misaligned, None, FAKE, ws, None)
+    assert rc == ra.ERR_INVALID_ARG
+    rc = L.ring_attn_ulysses_forward(ctypes.byref(ud), shards, shards, shards, shards, nulls, FAKE, ws, None)
+    assert rc == ra.ERR_INVALID_ARG
+    rc = L.ring_attn_ulysses_forward(ctypes.byref(ud), None, shards, shards, shards, None, FAKE, ws, None)
+    assert rc == ra.ERR_INVALID_ARG
 
 
 def test_partition_rejects_bad_input():
