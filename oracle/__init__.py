@@ -23,13 +23,18 @@ Sources (the pages and their sections):
 * Lecture 30 "TP/PP/SP/CP", section 3.2: causal masking is lower-triangular by
   global token position; section 3.4: the ring carries the small GQA KV heads.
 
+``backward.py`` adds the gradient of that attention with respect to Q, K
+and V (the pages give the forward only; see its docstring).
+
 Every function here is pinned by ``tests/test_oracle_*.py`` against closed
 forms, a library routine and invariants (see each function's docstring).
 """
 from .positions import device_positions, partition_table
 from .attention import attention_rows, device_share, visible_pair_count, kv_head_of
+from .backward import attention_backward_rows, device_backward, upstream_rows
 
 __all__ = [
     "device_positions", "partition_table", "attention_rows", "device_share",
-    "visible_pair_count", "kv_head_of",
+    "visible_pair_count", "kv_head_of", "attention_backward_rows", "device_backward",
+    "upstream_rows",
 ]

@@ -14,7 +14,9 @@ Generation recipe (the same for every workload):
   by ``SeedSequence([seed, tensor_id, b, h, chunk])``, in float32, so any
   chunk regenerates on its own and the result never depends on the order
   or the threads used to draw it.
-* Q and K are ``N(0, qk_std**2)``; V is ``N(0, 1)`` or ``U(-1, 1)``.
+* Q and K are ``N(0, qk_std**2)``; V is ``N(0, 1)`` or ``U(-1, 1)``; the
+  upstream gradient dO of the backward pass (tensor "do", query heads) is
+  ``N(0, 1)``.
 * For bf16 workloads every value is then rounded once to bfloat16
   (round-to-nearest-even); both sides consume the rounded values.
 * A duplicated-key fraction (the numerics-stress workload) copies K rows
@@ -30,7 +32,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-TENSOR_IDS = {"q": 0, "k": 1, "v": 2}
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "do": 3}
 _DUP_STREAM = 99
 
 
@@ -148,7 +150,7 @@ def _draw_chunk(wl: Workload, tensor: str, b: int, h: int, chunk: int) -> np.nda
     shape = (wl.gen_chunk, wl.head_dim)
     if tensor == "v" and wl.v_dist == "uniform":
         x = rng.uniform(-1.0, 1.0, size=shape).astype(np.float32)
-    elif tensor == "v":
+    elif tensor in ("v", "do"):
         x = rng.standard_normal(shape, dtype=np.float32)
     else:
         x = rng.standard_normal(shape, dtype=np.float32)
