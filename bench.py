@@ -232,6 +232,63 @@ def bench_ulysses(wl, rank, K, Wm):
     print(json.dumps(rec), flush=True)
 
 
+def bench_backward(wl, rank, K, Wm):
+    """One device's backward pass over the whole ring (ring_attn_backward):
+    row terms, one dQ and one dK/dV launch per step, dQ conversion. The
+    forward output and LSE it reads are computed once, outside the timing.
+    Effective FLOPs are the usual backward count, 10 * d * H_q * B per
+    visible pair (five products of the forward's size); the kernels execute
+    14 (S and dP are formed by both kernels)."""
+    import torch
+    import ring_attention_blockwise_amd as ra
+    from ring_attention_blockwise_amd import harness
+
+    dev = torch.device("cuda:0")
+    share = harness.build_share(wl, rank, dev)
+    copy_stream = torch.cuda.Stream()
+    out, lse = harness.run_forward(share, copy_stream=copy_stream)
+    d_out = harness.build_upstream(share)
+    dk, dv = harness.new_kv_grads(share)
+    ws = torch.empty(ra.backward_workspace_size(share.ring_desc()), dtype=torch.uint8, device=dev)
+    pairs = harness.step_pairs(wl, rank)
+    launched = [s for s in range(wl.world) if pairs[s] > 0]
+    per_pair = 10.0 * wl.head_dim * wl.heads_q * wl.batch
+    total_flops = per_pair * sum(pairs)
+    events = [ra.StepEvents(2 * wl.world) for _ in range(K)]
+    cur = torch.cuda.current_stream()
+    for _ in range(Wm):
+        harness.run_backward(share, out, lse, d_out, dk, dv, copy_stream=copy_stream, workspace=ws)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(cur)
+    for i in range(K):
+        harness.run_backward(share, out, lse, d_out, dk, dv, copy_stream=copy_stream, workspace=ws,
+                             step_events=events[i])
+    stop.record(cur)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / K
+    step_ms = sum(ev.elapsed_ms(2 * s, 2 * s + 1) for ev in events for s in launched) / (K * len(launched))
+    flops_per_step = per_pair * sum(pairs[s] for s in launched) / len(launched)
+    achieved = flops_per_step / (step_ms * 1e-3) / 1e12
+    value = total_flops / (ms * 1e-3) / 1e12
+    rec = {
+        "metric": "effective causal attention-backward TFLOP/s of one device's ring share at 1 GPU",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": Wm,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic (seeded N(0,1) Q/K/V/dO, bf16-rounded)",
+        "config": {"workload": wl.name, "pass": "backward", "description": wl.description, "batch": wl.batch,
+                   "heads_q": wl.heads_q, "heads_kv": wl.heads_kv, "head_dim": wl.head_dim,
+                   "local_len": wl.local_len, "world": wl.world, "rank": rank, "partition": wl.partition},
+        "effective_tflop_per_backward": round(total_flops / 1e12, 4),
+        "step_kernels": {"launch_pairs_per_backward": len(launched), "avg_step_ms": round(step_ms, 4),
+                         "tflops": round(achieved, 2),
+                         "executed_mfma_tflops": round(achieved * 1.4, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -240,6 +297,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--rank", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass of the workload's share instead of the forward")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -263,6 +322,9 @@ def main():
         return
     wl = ring_inputs.WORKLOADS[args.workload]
     rank = wl.ranks[0] if args.rank is None else args.rank
+    if args.backward:
+        bench_backward(wl, rank, args.steps, args.warmup)
+        return
     dev = torch.device("cuda:0")
     t0 = time.time()
     share = harness.build_share(wl, rank, dev)

@@ -223,6 +223,69 @@ int ring_attn_ulysses_forward(const ra_ulysses_desc* desc, const void* const* q_
                               void* const* out_shards, float* const* lse_shards,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- backward ring step (gradients) --------------------------------------- */
+
+/* The pages run the ring forward only ([HC] 6.2 has no backward pass). The
+ * backward step is the plain extension of the same block step: with the
+ * forward's LSE and P_ij = exp(scale q_i.k_j - LSE_i) over the visible keys,
+ * D_i = dO_i . O_i and dS_ij = P_ij (dO_i . v_j - D_i),
+ *   dQ_i += scale sum_j dS_ij k_j,   dK_j += scale sum_i dS_ij q_i,
+ *   dV_j += sum_i P_ij dO_i,
+ * i over the local query rows, j over the keys of one K/V block. dQ stays on
+ * the device; dK and dV are accumulators that travel around the ring with
+ * their K/V block and are back at the block's owner after a full turn.
+ * Built for RA_BF16 with head_dim 128 (other shapes: RA_ERR_UNSUPPORTED). */
+
+#define RA_BWD_INIT_DQ 1          /* ring_attn_backward_step: dq_acc starts at 0 */
+
+/* Per-row terms every backward step reads, from the forward's output:
+ *   out, d_out [B, Hq, q_len, d] desc->dtype (O and the upstream gradient dO)
+ *   lse        [B, Hq, q_len]    fp32, natural log, as ring_attn_finalize writes
+ *   terms      [2, B, Hq, q_len] fp32, written: terms[r] = -LSE_r / scale
+ *              (-inf for a row with LSE = -inf), terms[R + r] = -(dO_r . O_r),
+ *              R = B * Hq * q_len.
+ * Uses batch, heads_q, q_len, head_dim, dtype and scale of desc (any dtype
+ * and head_dim the forward supports). */
+int ring_attn_backward_prep(const ra_step_desc* desc, const void* out, const void* d_out, const float* lse,
+                            float* terms, void* stream);
+
+/* One backward step: the gradient contributions of the local query rows
+ * against one K/V block (same descriptor as the forward step).
+ *   q          [B, Hq,  q_len,  d] bf16    read
+ *   k, v       [B, Hkv, kv_len, d] bf16    read
+ *   d_out      [B, Hq,  q_len,  d] bf16    read
+ *   terms      as ring_attn_backward_prep wrote them               read
+ *   dq_acc     [B, Hq,  q_len,  d] fp32    read (unless RA_BWD_INIT_DQ) and written
+ *   dk_acc, dv_acc [B, Hkv, kv_len, d] fp32  read and written (accumulated)
+ *   flags      0 or RA_BWD_INIT_DQ.
+ * Keys that no local row sees are left untouched; so are rows that see no
+ * key of the block (set to 0 with RA_BWD_INIT_DQ). */
+int ring_attn_backward_step(const ra_step_desc* desc, const void* q, const void* k, const void* v,
+                            const void* d_out, const float* terms, float* dq_acc, float* dk_acc, float* dv_acc,
+                            int32_t flags, void* stream);
+
+/* Bytes of workspace ring_attn_backward needs: two receive slots, the fp32
+ * dQ accumulator and the row terms. 0 on a bad desc. */
+size_t ring_attn_backward_workspace_size(const ra_ring_desc* desc);
+
+/* The backward pass of one device's share of a simulated ring: the row
+ * terms, then n backward steps in the forward's block order, then dQ in the
+ * input dtype.
+ *   q_local, k_blocks, v_blocks, step_events, streams  as ring_attn_forward
+ *                  (K/V blocks are received into workspace slots the same way).
+ *   out, lse       the forward's output [B, Hq, c, d] and LSE [B, Hq, c].
+ *   d_out          [B, Hq, c, d] the upstream gradient of out.
+ *   dq             [B, Hq, c, d] written, input dtype.
+ *   dk_acc[j], dv_acc[j]  HOST arrays of `world` DEVICE pointers, fp32
+ *                  [B, Hkv, c, d]: the accumulators travelling with block j;
+ *                  this device adds its contribution to every block's pair.
+ *                  Starting them at zero and running every rank leaves the
+ *                  full dK_j, dV_j in them. */
+int ring_attn_backward(const ra_ring_desc* desc, const void* q_local, const void* const* k_blocks,
+                       const void* const* v_blocks, const void* out, const void* d_out, const float* lse, void* dq,
+                       float* const* dk_acc, float* const* dv_acc, void* workspace, size_t workspace_bytes,
+                       void* compute_stream, void* copy_stream, void* const* step_events);
+
 /* ---- host-only helpers (no device work) ---------------------------------- */
 
 /* Segments of device `rank`'s local rows under `partition` (RA_PART_*).

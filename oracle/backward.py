@@ -37,7 +37,10 @@ def attention_backward_rows(q, q_pos, k, v, k_pos, do, causal: bool, scale: floa
     ``do`` [R, dv] is the gradient of the loss with respect to the output.
     Returns a dict: ``dq`` [R, d], ``dk`` [L, d], ``dv`` [L, dv] (the part of
     the key/value gradients that these rows produce), ``out`` [R, dv],
-    ``lse`` [R] and ``delta`` [R] (= D_i).
+    ``lse`` [R] and ``delta`` [R] (= D_i). Two more row terms size the
+    rounding error a reduced-precision evaluation of dQ can make (they are
+    not gradients): ``p_k`` [R, d] = sum_j P_ij k_j (the attention output
+    with the keys as values) and ``abs_ds_k`` [R, d] = sum_j |dS_ij| |k_j|.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -60,7 +63,8 @@ def attention_backward_rows(q, q_pos, k, v, k_pos, do, causal: bool, scale: floa
     ds = p * (dp - delta[:, None])
     dq = scale * (ds @ k)
     dk = scale * (ds.T @ q)
-    return {"dq": dq, "dk": dk, "dv": dv, "out": out, "lse": lse, "delta": delta}
+    return {"dq": dq, "dk": dk, "dv": dv, "out": out, "lse": lse, "delta": delta,
+            "p_k": p @ k, "abs_ds_k": np.abs(ds) @ np.abs(k)}
 
 
 def upstream_rows(wl: "ring_inputs.Workload", b: int, h: int, positions) -> np.ndarray:

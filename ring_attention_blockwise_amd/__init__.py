@@ -23,6 +23,7 @@ F32, BF16 = 0, 1
 CONTIGUOUS, ZIGZAG, STRIPED = 0, 1, 2
 PARTITIONS = {"contiguous": CONTIGUOUS, "zigzag": ZIGZAG, "striped": STRIPED}
 STEP_INIT = 1
+BWD_INIT_DQ = 1
 
 EXPORTED = (
     "ring_attn_step", "ring_attn_merge", "ring_attn_finalize", "ring_attn_forward_workspace_size",
@@ -30,6 +31,8 @@ EXPORTED = (
     "ring_attn_visible_pairs", "ring_attn_last_error", "ring_attn_abi_version",
     "ring_attn_events_create", "ring_attn_event_elapsed_ms", "ring_attn_events_destroy",
     "ring_attn_synchronize", "ring_attn_ulysses_workspace_size", "ring_attn_ulysses_forward",
+    "ring_attn_backward_prep", "ring_attn_backward_step", "ring_attn_backward_workspace_size",
+    "ring_attn_backward",
 )
 
 
@@ -102,6 +105,10 @@ def lib() -> ctypes.CDLL:
             "ring_attn_synchronize": (ctypes.c_int, [P]),
             "ring_attn_ulysses_workspace_size": (SZ, [UD]),
             "ring_attn_ulysses_forward": (ctypes.c_int, [UD, P, P, P, P, P, P, SZ, P]),
+            "ring_attn_backward_prep": (ctypes.c_int, [SD, P, P, P, P, P]),
+            "ring_attn_backward_step": (ctypes.c_int, [SD, P, P, P, P, P, P, P, P, I32, P]),
+            "ring_attn_backward_workspace_size": (SZ, [RD]),
+            "ring_attn_backward": (ctypes.c_int, [RD, P, P, P, P, P, P, P, P, P, P, SZ, P, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -313,6 +320,75 @@ def ulysses_forward(ud: UlyssesDesc, q_shards: Sequence, k_shards: Sequence, v_s
     ws = _ptr(workspace, torch.uint8, (workspace.numel(),), "workspace")
     _check(lib().ring_attn_ulysses_forward(ctypes.byref(ud), qp, kp, vp, op, lp, ws, workspace.numel(),
                                            _stream(stream)), "ring_attn_ulysses_forward")
+
+
+def backward_prep(sd: StepDesc, out, d_out, lse, terms, stream=None):
+    """Row terms of the backward step (ring_attn_backward_prep); ``terms`` is
+    fp32 [2, B, Hq, q_len]."""
+    torch = _torch()
+    dt = _dtype_of(sd.dtype)
+    B, Hq, D, S = sd.batch, sd.heads_q, sd.head_dim, sd.q_len
+    f = torch.float32
+    _check(lib().ring_attn_backward_prep(
+        ctypes.byref(sd), _ptr(out, dt, (B, Hq, S, D), "out"), _ptr(d_out, dt, (B, Hq, S, D), "d_out"),
+        _ptr(lse, f, (B, Hq, S), "lse"), _ptr(terms, f, (2, B, Hq, S), "terms"), _stream(stream)),
+        "ring_attn_backward_prep")
+
+
+def backward_step(sd: StepDesc, q, k, v, d_out, terms, dq_acc, dk_acc, dv_acc, init_dq: bool = False,
+                  stream=None):
+    """Add one K/V block's gradient contributions (ring_attn_backward_step)."""
+    torch = _torch()
+    dt = _dtype_of(sd.dtype)
+    f = torch.float32
+    B, Hq, Hk, D = sd.batch, sd.heads_q, sd.heads_kv, sd.head_dim
+    args = (
+        _ptr(q, dt, (B, Hq, sd.q_len, D), "q"), _ptr(k, dt, (B, Hk, sd.kv_len, D), "k"),
+        _ptr(v, dt, (B, Hk, sd.kv_len, D), "v"), _ptr(d_out, dt, (B, Hq, sd.q_len, D), "d_out"),
+        _ptr(terms, f, (2, B, Hq, sd.q_len), "terms"), _ptr(dq_acc, f, (B, Hq, sd.q_len, D), "dq_acc"),
+        _ptr(dk_acc, f, (B, Hk, sd.kv_len, D), "dk_acc"), _ptr(dv_acc, f, (B, Hk, sd.kv_len, D), "dv_acc"),
+    )
+    _check(lib().ring_attn_backward_step(ctypes.byref(sd), *args, BWD_INIT_DQ if init_dq else 0, _stream(stream)),
+           "ring_attn_backward_step")
+
+
+def backward_workspace_size(rd: RingDesc) -> int:
+    n = lib().ring_attn_backward_workspace_size(ctypes.byref(rd))
+    if n == 0:
+        raise RingAttnError(ERR_INVALID_ARG, f"backward_workspace_size: {last_error()}")
+    return int(n)
+
+
+def backward(rd: RingDesc, q_local, k_blocks: Sequence, v_blocks: Sequence, out, d_out, lse, dq,
+             dk_acc: Sequence, dv_acc: Sequence, workspace, compute_stream=None, copy_stream=None,
+             step_events: Optional["StepEvents"] = None):
+    """One device's backward pass over the whole ring (ring_attn_backward): writes
+    ``dq`` and adds this device's contributions to the fp32 accumulators
+    ``dk_acc[j]``, ``dv_acc[j]`` of every block j."""
+    torch = _torch()
+    dt = _dtype_of(rd.dtype)
+    f = torch.float32
+    B, Hq, Hk, D, c, n = rd.batch, rd.heads_q, rd.heads_kv, rd.head_dim, rd.local_len, rd.world
+    for name, arr in (("k_blocks", k_blocks), ("v_blocks", v_blocks), ("dk_acc", dk_acc), ("dv_acc", dv_acc)):
+        if len(arr) != n:
+            raise ValueError(f"need {n} {name}")
+
+    def ptrs(arr, dtype, name):
+        return (ctypes.c_void_p * n)(*[_ptr(t, dtype, (B, Hk, c, D), f"{name}[{i}]").value
+                                      for i, t in enumerate(arr)])
+
+    ev = None
+    if step_events is not None:
+        if step_events.n != 2 * n:
+            raise ValueError("step_events must hold 2 * world events")
+        ev = step_events.array
+    ws = _ptr(workspace, torch.uint8, (workspace.numel(),), "workspace")
+    _check(lib().ring_attn_backward(
+        ctypes.byref(rd), _ptr(q_local, dt, (B, Hq, c, D), "q_local"), ptrs(k_blocks, dt, "k_blocks"),
+        ptrs(v_blocks, dt, "v_blocks"), _ptr(out, dt, (B, Hq, c, D), "out"), _ptr(d_out, dt, (B, Hq, c, D), "d_out"),
+        _ptr(lse, f, (B, Hq, c), "lse"), _ptr(dq, dt, (B, Hq, c, D), "dq"), ptrs(dk_acc, f, "dk_acc"),
+        ptrs(dv_acc, f, "dv_acc"), ws, workspace.numel(), _stream(compute_stream),
+        None if copy_stream is None else ctypes.c_void_p(copy_stream.cuda_stream), ev), "ring_attn_backward")
 
 
 class StepEvents:

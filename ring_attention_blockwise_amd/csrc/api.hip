@@ -10,6 +10,7 @@
 #include <cstring>
 #include <vector>
 
+#include "backward.h"
 #include "common.h"
 #include "ring_attn.h"
 
@@ -217,7 +218,7 @@ extern "C" {
 
 const char* ring_attn_last_error(void) { return g_last_error; }
 
-int32_t ring_attn_abi_version(void) { return 101; }
+int32_t ring_attn_abi_version(void) { return 102; }
 
 int ring_attn_partition_segments(int32_t partition, int32_t world, int32_t rank, int64_t local_len,
                                  ra_segment* segs, int32_t* n_segs) {
@@ -670,6 +671,235 @@ int ring_attn_ulysses_forward(const ra_ulysses_desc* d, const void* const* q_sha
                             (size_t)L.ls * 4, (size_t)d->seq_len * 4, s)) != hipSuccess)
       return hip_fail(e, "ulysses scatter (lse)");
   }
+  return RA_OK;
+}
+
+/* ---- backward ------------------------------------------------------------ */
+
+namespace {
+
+float scale_of(const ra_step_desc* d) {
+  return d->scale > 0.0f ? d->scale : (float)(1.0 / std::sqrt((double)d->head_dim));
+}
+
+// The backward kernels are built for bf16 with head_dim 128.
+int check_backward_shape(const ra_step_desc* d) {
+  int rc = check_shape(d, true);
+  if (rc) return rc;
+  if (d->dtype != RA_BF16 || d->head_dim != 128)
+    return fail(RA_ERR_UNSUPPORTED, "the backward step is built for bf16 with head_dim 128");
+  return RA_OK;
+}
+
+struct BwdLayout {
+  size_t block_bytes, rows;
+  size_t off_slot[2][2];
+  size_t off_dq, off_terms, total;
+};
+
+void bwd_layout(const ra_ring_desc* d, BwdLayout* L) {
+  const size_t es = d->dtype == RA_BF16 ? 2 : 4;
+  L->block_bytes = (size_t)d->batch * d->heads_kv * (size_t)d->local_len * d->head_dim * es;
+  L->rows = (size_t)d->batch * d->heads_q * (size_t)d->local_len;
+  size_t off = 0;
+  for (int s = 0; s < 2; ++s)
+    for (int t = 0; t < 2; ++t) {
+      L->off_slot[s][t] = off;
+      off += align256(L->block_bytes);
+    }
+  L->off_dq = off;
+  off += align256(L->rows * d->head_dim * 4);
+  L->off_terms = off;
+  off += align256(L->rows * 2 * 4);
+  L->total = off + 256;
+}
+
+}  // namespace
+
+int ring_attn_backward_prep(const ra_step_desc* d, const void* out, const void* d_out, const float* lse,
+                            float* terms, void* stream) {
+  int rc = check_shape(d, false);
+  if (rc) return rc;
+  const int64_t rows = (int64_t)d->batch * d->heads_q * d->q_len;
+  if (rows == 0) return RA_OK;
+  if (!out || !d_out || !lse || !terms) return fail(RA_ERR_INVALID_ARG, "out/d_out/lse/terms must not be NULL");
+  hipError_t e = ra::launch_bwd_prep(out, d_out, lse, terms, rows, d->head_dim, d->dtype, scale_of(d),
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RA_OK : hip_fail(e, "backward prep launch");
+}
+
+int ring_attn_backward_step(const ra_step_desc* d, const void* q, const void* k, const void* v, const void* d_out,
+                            const float* terms, float* dq_acc, float* dk_acc, float* dv_acc, int32_t flags,
+                            void* stream) {
+  int rc = check_backward_shape(d);
+  if (rc) return rc;
+  if (d->causal != 0 && d->causal != 1) return fail(RA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  rc = check_segments(d->q_seg, d->n_q_seg, d->q_len, d->causal, "q");
+  if (rc) return rc;
+  rc = check_segments(d->kv_seg, d->n_kv_seg, d->kv_len, d->causal, "kv");
+  if (rc) return rc;
+  if (flags & ~RA_BWD_INIT_DQ) return fail(RA_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  const bool has_rows = d->q_len > 0 && d->batch > 0;
+  if (!has_rows) return RA_OK;
+  if (!q || !d_out || !terms || !dq_acc) return fail(RA_ERR_INVALID_ARG, "q/d_out/terms/dq_acc must not be NULL");
+  if (d->kv_len > 0 && (!k || !v || !dk_acc || !dv_acc))
+    return fail(RA_ERR_INVALID_ARG, "k/v/dk_acc/dv_acc must not be NULL");
+  if (!aligned16(q) || !aligned16(d_out) || !aligned16(dq_acc) || (k && !aligned16(k)) || (v && !aligned16(v)) ||
+      (dk_acc && !aligned16(dk_acc)) || (dv_acc && !aligned16(dv_acc)) || !aligned16(terms))
+    return fail(RA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool init = flags & RA_BWD_INIT_DQ;
+  hipError_t e;
+  if (pairs_of(d) == 0) {
+    if (!init) return RA_OK;
+    e = ra::launch_zero(dq_acc, (size_t)d->batch * d->heads_q * d->q_len * d->head_dim * 4, s);
+    return e == hipSuccess ? RA_OK : hip_fail(e, "dq clear");
+  }
+  ra::BwdArgs a{};
+  a.s = make_args(d);
+  a.s.q = q;
+  a.s.k = k;
+  a.s.v = v;
+  a.dout = d_out;
+  a.terms = terms;
+  a.dq = dq_acc;
+  a.dk = dk_acc;
+  a.dv = dv_acc;
+  a.scale = scale_of(d);
+  a.init_dq = init;
+  e = ra::launch_bwd_bf16(a, d->head_dim, s);
+  return e == hipSuccess ? RA_OK : hip_fail(e, "backward step launch");
+}
+
+size_t ring_attn_backward_workspace_size(const ra_ring_desc* d) {
+  if (check_ring_desc(d) != RA_OK) return 0;
+  BwdLayout L;
+  bwd_layout(d, &L);
+  return L.total;
+}
+
+int ring_attn_backward(const ra_ring_desc* d, const void* q_local, const void* const* k_blocks,
+                       const void* const* v_blocks, const void* out, const void* d_out, const float* lse, void* dq,
+                       float* const* dk_acc, float* const* dv_acc, void* workspace, size_t workspace_bytes,
+                       void* compute_stream, void* copy_stream, void* const* step_events) {
+  int rc = check_ring_desc(d);
+  if (rc) return rc;
+  if (d->dtype != RA_BF16 || d->head_dim != 128)
+    return fail(RA_ERR_UNSUPPORTED, "the backward step is built for bf16 with head_dim 128");
+  const int n = d->world;
+  const bool has_rows = d->local_len > 0 && d->batch > 0;
+  if (!k_blocks || !v_blocks || !dk_acc || !dv_acc)
+    return fail(RA_ERR_INVALID_ARG, "k_blocks/v_blocks/dk_acc/dv_acc must not be NULL");
+  if (has_rows) {
+    if (!q_local || !out || !d_out || !lse || !dq) return fail(RA_ERR_INVALID_ARG, "q/out/d_out/lse/dq must not be NULL");
+    if (!aligned16(q_local) || !aligned16(out) || !aligned16(d_out) || !aligned16(dq))
+      return fail(RA_ERR_INVALID_ARG, "q/out/d_out/dq must be 16-byte aligned");
+    for (int j = 0; j < n; ++j) {
+      if (!k_blocks[j] || !v_blocks[j] || !dk_acc[j] || !dv_acc[j])
+        return fail(RA_ERR_INVALID_ARG, "block %d pointer is NULL", j);
+      if (!aligned16(k_blocks[j]) || !aligned16(v_blocks[j]) || !aligned16(dk_acc[j]) || !aligned16(dv_acc[j]))
+        return fail(RA_ERR_INVALID_ARG, "block %d is not 16-byte aligned", j);
+    }
+  }
+  if (step_events)
+    for (int i = 0; i < 2 * n; ++i)
+      if (!step_events[i]) return fail(RA_ERR_INVALID_ARG, "step_events[%d] is NULL", i);
+  BwdLayout L;
+  bwd_layout(d, &L);
+  if (workspace == nullptr || workspace_bytes < L.total)
+    return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, workspace_bytes);
+  if (copy_stream != nullptr && copy_stream == compute_stream)
+    return fail(RA_ERR_INVALID_ARG, "copy_stream must differ from compute_stream (or be NULL)");
+  if (!has_rows) return RA_OK;
+
+  std::vector<ra_step_desc> steps(n);
+  std::vector<int32_t> owner(n);
+  std::vector<int64_t> pairs(n);
+  int first = -1;
+  for (int s = 0; s < n; ++s) {
+    rc = ring_attn_ring_step_desc(d, s, &steps[s], &owner[s]);
+    if (rc) return rc;
+    pairs[s] = pairs_of(&steps[s]);
+    if (pairs[s] > 0 && first < 0) first = s;
+  }
+
+  char* base = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~(uintptr_t)255);
+  void* slot_k[2] = {base + L.off_slot[0][0], base + L.off_slot[1][0]};
+  void* slot_v[2] = {base + L.off_slot[0][1], base + L.off_slot[1][1]};
+  float* dq_acc = reinterpret_cast<float*>(base + L.off_dq);
+  float* terms = reinterpret_cast<float*>(base + L.off_terms);
+
+  hipStream_t cs = static_cast<hipStream_t>(compute_stream);
+  hipStream_t xs = copy_stream ? static_cast<hipStream_t>(copy_stream) : cs;
+  DriverEvents* ev = nullptr;
+  hipError_t e = driver_events(&ev);
+  if (e != hipSuccess) return hip_fail(e, "event creation");
+  bool freed_recorded[2] = {false, false};
+  if (xs != cs && n > 1) {
+    if ((e = hipEventRecord(ev->freed[0], cs)) != hipSuccess) return hip_fail(e, "event record");
+    if ((e = hipStreamWaitEvent(xs, ev->freed[0], 0)) != hipSuccess) return hip_fail(e, "stream wait");
+  }
+  auto enqueue_receive = [&](int s) -> hipError_t {
+    const int slot = s & 1;
+    hipError_t err;
+    if (freed_recorded[slot] && xs != cs)
+      if ((err = hipStreamWaitEvent(xs, ev->freed[slot], 0)) != hipSuccess) return err;
+    if ((err = hipMemcpyAsync(slot_k[slot], k_blocks[owner[s]], L.block_bytes, hipMemcpyDeviceToDevice, xs)) !=
+        hipSuccess)
+      return err;
+    if ((err = hipMemcpyAsync(slot_v[slot], v_blocks[owner[s]], L.block_bytes, hipMemcpyDeviceToDevice, xs)) !=
+        hipSuccess)
+      return err;
+    return hipEventRecord(ev->ready[slot], xs);
+  };
+
+  const float scale = d->scale > 0.0f ? d->scale : (float)(1.0 / std::sqrt((double)d->head_dim));
+  if ((e = ra::launch_bwd_prep(out, d_out, lse, terms, (int64_t)L.rows, d->head_dim, d->dtype, scale, cs)) !=
+      hipSuccess)
+    return hip_fail(e, "backward prep launch");
+  for (int s = 0; s < n; ++s) {
+    if (s + 1 < n)
+      if ((e = enqueue_receive(s + 1)) != hipSuccess) return hip_fail(e, "receive copy");
+    const void* kb = k_blocks[owner[s]];
+    const void* vb = v_blocks[owner[s]];
+    if (s > 0) {
+      kb = slot_k[s & 1];
+      vb = slot_v[s & 1];
+      if (xs != cs)
+        if ((e = hipStreamWaitEvent(cs, ev->ready[s & 1], 0)) != hipSuccess) return hip_fail(e, "stream wait");
+    }
+    if (step_events)
+      if ((e = hipEventRecord(static_cast<hipEvent_t>(step_events[2 * s]), cs)) != hipSuccess)
+        return hip_fail(e, "step event");
+    if (pairs[s] > 0) {
+      ra::BwdArgs a{};
+      a.s = make_args(&steps[s]);
+      a.s.q = q_local;
+      a.s.k = kb;
+      a.s.v = vb;
+      a.dout = d_out;
+      a.terms = terms;
+      a.dq = dq_acc;
+      a.dk = dk_acc[owner[s]];
+      a.dv = dv_acc[owner[s]];
+      a.scale = scale;
+      a.init_dq = (s == first);
+      if ((e = ra::launch_bwd_bf16(a, d->head_dim, cs)) != hipSuccess) return hip_fail(e, "backward step launch");
+    }
+    if (step_events)
+      if ((e = hipEventRecord(static_cast<hipEvent_t>(step_events[2 * s + 1]), cs)) != hipSuccess)
+        return hip_fail(e, "step event");
+    if (s > 0 && xs != cs) {
+      if ((e = hipEventRecord(ev->freed[s & 1], cs)) != hipSuccess) return hip_fail(e, "event record");
+      freed_recorded[s & 1] = true;
+    }
+  }
+  const int64_t n_dq = (int64_t)L.rows * d->head_dim;
+  if (first < 0) {
+    if ((e = ra::launch_zero(dq, (size_t)n_dq * 2, cs)) != hipSuccess) return hip_fail(e, "dq clear");
+    return RA_OK;
+  }
+  if ((e = ra::launch_convert(dq_acc, dq, n_dq, d->dtype, cs)) != hipSuccess) return hip_fail(e, "dq convert");
   return RA_OK;
 }
 

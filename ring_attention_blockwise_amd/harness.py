@@ -12,8 +12,8 @@ import dataclasses
 import numpy as np
 
 import ring_inputs
-from . import (BF16, F32, RingDesc, finalize, forward, forward_workspace_size, partition_segments,
-               ring_desc, ring_step_desc, step, visible_pairs)
+from . import (BF16, F32, RingDesc, backward, backward_workspace_size, finalize, forward,
+               forward_workspace_size, partition_segments, ring_desc, ring_step_desc, step, visible_pairs)
 
 
 def positions(segs) -> np.ndarray:
@@ -180,3 +180,38 @@ def step_pairs(wl: ring_inputs.Workload, rank: int):
     """Visible (query, key) pairs per (batch, head) of every ring step of a share."""
     rd = make_ring_desc(wl, rank)
     return [visible_pairs(ring_step_desc(rd, s)[0]) for s in range(wl.world)]
+
+
+def build_upstream(share: DeviceShare):
+    """The seeded upstream gradient dO at the device's rows, [B, Hq, c, d] on the GPU."""
+    import torch
+    wl = share.workload
+    dt = torch_dtype(wl)
+    d_out = torch.empty_like(share.q)
+    for b in range(wl.batch):
+        for h in range(wl.heads_q):
+            d_out[b, h] = _to_device(ring_inputs.rows(wl, "do", b, h, share.q_positions), dt, share.q.device)
+    return d_out
+
+
+def new_kv_grads(share: DeviceShare):
+    """Zeroed fp32 dK and dV accumulators, one pair per K/V block."""
+    import torch
+    wl = share.workload
+    shape = (wl.batch, wl.heads_kv, wl.local_len, wl.head_dim)
+    dk = [torch.zeros(shape, dtype=torch.float32, device=share.q.device) for _ in range(wl.world)]
+    dv = [torch.zeros(shape, dtype=torch.float32, device=share.q.device) for _ in range(wl.world)]
+    return dk, dv
+
+
+def run_backward(share: DeviceShare, out, lse, d_out, dk_acc, dv_acc, copy_stream=None, workspace=None,
+                 step_events=None):
+    """ring_attn_backward on the current stream; returns dQ (input dtype)."""
+    import torch
+    rd = share.ring_desc()
+    if workspace is None:
+        workspace = torch.empty(backward_workspace_size(rd), dtype=torch.uint8, device=share.q.device)
+    dq = torch.empty_like(share.q)
+    backward(rd, share.q, share.k_blocks, share.v_blocks, out, d_out, lse, dq, dk_acc, dv_acc, workspace,
+             copy_stream=copy_stream, step_events=step_events)
+    return dq

@@ -129,6 +129,29 @@ ULYSSES_WORKLOADS = {
 }
 
 
+# Backward-pass workloads (small enough for the oracle to cover every row):
+# GQA zigzag, two batches striped, non-causal, and ragged row counts.
+BACKWARD_WORKLOADS = {
+    "bwd_zigzag4k_4dev_gqa": Workload(
+        name="bwd_zigzag4k_4dev_gqa", batch=1, heads_q=8, heads_kv=2, head_dim=128, dtype="bf16",
+        causal=True, partition="zigzag", world=4, local_len=1024, seed=1008, ranks=(0, 1, 2, 3),
+        description="backward, causal zigzag, 4096 tokens over 4 devices, 8 Q / 2 KV heads, d128 bf16"),
+    "bwd_striped2k_2dev_b2": Workload(
+        name="bwd_striped2k_2dev_b2", batch=2, heads_q=4, heads_kv=4, head_dim=128, dtype="bf16",
+        causal=True, partition="striped", world=2, local_len=1024, seed=1009, ranks=(0, 1),
+        description="backward, causal striped, 2048 tokens over 2 devices, B2, H4, d128 bf16"),
+    "bwd_noncausal1k_4dev": Workload(
+        name="bwd_noncausal1k_4dev", batch=1, heads_q=4, heads_kv=2, head_dim=128, dtype="bf16",
+        causal=False, partition="contiguous", world=4, local_len=256, seed=1010, ranks=(0, 1, 2, 3),
+        description="backward, non-causal, 1024 tokens over 4 devices, 4 Q / 2 KV heads, d128 bf16"),
+    "bwd_ragged3k_3dev": Workload(
+        name="bwd_ragged3k_3dev", batch=1, heads_q=4, heads_kv=1, head_dim=128, dtype="bf16",
+        causal=True, partition="zigzag", world=3, local_len=1000, seed=1011, ranks=(0, 1, 2),
+        description="backward, causal zigzag, 3000 tokens over 3 devices (ragged tiles), 4 Q / 1 KV head, "
+                    "d128 bf16"),
+}
+
+
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even); float32 out."""
     x = np.ascontiguousarray(x, dtype=np.float32)

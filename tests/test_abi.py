@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert ra.lib().ring_attn_abi_version() == 101
+    assert ra.lib().ring_attn_abi_version() == 102
 
 
 def _expand(segs):
@@ -193,6 +193,38 @@ def test_ulysses_workspace_and_validation():
     assert rc == ra.ERR_INVALID_ARG
     rc = L.ring_attn_ulysses_forward(ctypes.byref(ud), None, shards, shards, shards, None, FAKE, ws, None)
     assert rc == ra.ERR_INVALID_ARG
+
+
+def test_backward_workspace_and_validation():
+    """The backward entry points check every argument on the host: unsupported
+    shapes, bad flags, NULL or misaligned pointers and a small workspace are
+    rejected before anything is enqueued."""
+    L = ra.lib()
+    rd = ra.ring_desc(1, 8, 2, 128, 1024, 4, 1, partition="zigzag")
+    ws = ra.backward_workspace_size(rd)
+    block = 2 * 1024 * 128 * 2
+    rows = 8 * 1024
+    assert ws >= 4 * block + rows * 128 * 4 + 2 * rows * 4
+    blocks = (ctypes.c_void_p * 4)(*([0x10000] * 4))
+    args = (FAKE, blocks, blocks, FAKE, FAKE, FAKE, FAKE, blocks, blocks)
+    assert L.ring_attn_backward(ctypes.byref(rd), *args, FAKE, ws - 1, None, None, None) == ra.ERR_WORKSPACE
+    nulls = (ctypes.c_void_p * 4)(*([0x10000] * 3 + [None]))
+    assert L.ring_attn_backward(ctypes.byref(rd), FAKE, blocks, blocks, FAKE, FAKE, FAKE, FAKE, blocks, nulls,
+                                FAKE, ws, None, None, None) == ra.ERR_INVALID_ARG
+    for bad in (ra.ring_desc(1, 8, 2, 64, 1024, 4, 1), ra.ring_desc(1, 8, 2, 128, 1024, 4, 1, dtype=ra.F32)):
+        assert L.ring_attn_backward(ctypes.byref(bad), *args, FAKE, 1 << 40, None, None, None) == ra.ERR_UNSUPPORTED
+    sd = ra.step_desc(1, 8, 2, 128, 256, 256, causal=False)
+    step_args = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert L.ring_attn_backward_step(ctypes.byref(sd), *step_args, 2, None) == ra.ERR_INVALID_ARG
+    assert L.ring_attn_backward_step(ctypes.byref(sd), None, *step_args[1:], 0, None) == ra.ERR_INVALID_ARG
+    mis = ctypes.c_void_p(0x10008)
+    assert L.ring_attn_backward_step(ctypes.byref(sd), *step_args[:5], mis, *step_args[6:], 0,
+                                     None) == ra.ERR_INVALID_ARG
+    sd64 = ra.step_desc(1, 8, 2, 64, 256, 256, causal=False)
+    assert L.ring_attn_backward_step(ctypes.byref(sd64), *step_args, 0, None) == ra.ERR_UNSUPPORTED
+    assert L.ring_attn_backward_prep(ctypes.byref(sd), None, FAKE, FAKE, FAKE, None) == ra.ERR_INVALID_ARG
+    causal_no_segments = ra.step_desc(1, 8, 2, 128, 256, 256)
+    assert L.ring_attn_backward_step(ctypes.byref(causal_no_segments), *step_args, 0, None) == ra.ERR_INVALID_ARG
 
 
 def test_partition_rejects_bad_input():

@@ -1,0 +1,187 @@
+"""GPU tests of the backward ring step against the oracle's gradients.
+
+The small workloads run the forward and then the backward of every device
+(the dK/dV accumulators of each block are shared by all devices, as they
+would be after travelling the whole ring) and compare every element of dQ,
+dK and dV with the oracle's gradient of full attention. A manual loop of
+ring_attn_backward_step must give the driver's result bit for bit. The 128K
+GQA share runs in the benchmark's configuration and compares a seeded sample
+of dQ rows (tile and chunk boundaries included) with the oracle, and checks
+two identities that hold at any size for one device's dK/dV contribution:
+sum over keys of dK = 0 and sum over keys of dV = sum over its rows of dO.
+
+Tolerance (bf16 path): the kernels round P and dS to bf16 (relative error
+2^-9 each) for the matrix products, and the row terms come from the bf16
+forward output (O rounded to bf16, LSE within 1e-3). On the small workloads
+errors are measured as max |GPU - oracle| / max |oracle| per tensor and must
+stay below 2e-2, the forward's output tolerance. On the long rows of the 128K
+share, D_i = dO_i . O_i computed from the bf16 output can cancel against
+dP_ij (|D_i| up to ~30 next to |dQ_i| ~ 0.01), so dQ is held to a per-element
+budget derived from those two roundings:
+  scale (2^-7 A_i |sum_j P_ij k_j| + 2^-8 sum_j |dS_ij| |k_j|) + 2^-8 |dQ_i| + 1e-4,
+with A_i = sum_d |dO_id| |O_id| bounding |D_i - D~_i| / 2^-7 (O off by at
+most 2^-8 relative: its own bf16 rounding plus the forward's)."""
+import numpy as np
+import pytest
+
+import oracle
+import ring_inputs
+import ring_attention_blockwise_amd as ra
+from ring_attention_blockwise_amd import harness
+
+pytestmark = pytest.mark.gpu
+
+TOL_REL = 2e-2
+BW = ring_inputs.BACKWARD_WORKLOADS
+
+
+def _copy_stream():
+    import torch
+    return torch.cuda.Stream()
+
+
+def _rel_err(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert np.isfinite(got).all()
+    return float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30))
+
+
+def _all_devices(wl):
+    import torch
+    dev = torch.device("cuda:0")
+    dk = dv = None
+    dqs, shares = [], []
+    for rank in range(wl.world):
+        share = harness.build_share(wl, rank, dev)
+        if dk is None:
+            dk, dv = harness.new_kv_grads(share)
+        cs = _copy_stream()
+        out, lse = harness.run_forward(share, copy_stream=cs)
+        d_out = harness.build_upstream(share)
+        dqs.append(harness.run_backward(share, out, lse, d_out, dk, dv, copy_stream=cs))
+        shares.append(share)
+    torch.cuda.synchronize()
+    return shares, dqs, dk, dv
+
+
+@pytest.mark.parametrize("name", list(BW) + ["zigzag8k_8dev_d128"])
+def test_small_backward_every_element(gpu, name):
+    wl = BW.get(name) or ring_inputs.WORKLOADS[name]
+    shares, dqs, dk, dv = _all_devices(wl)
+    full_dk = full_dv = 0.0
+    err_dq = 0.0
+    for rank in range(wl.world):
+        ref = oracle.device_backward(wl, rank)
+        full_dk = full_dk + ref["dk"]
+        full_dv = full_dv + ref["dv"]
+        err_dq = max(err_dq, _rel_err(dqs[rank].float().cpu().numpy(), ref["dq"]))
+    err_dk = err_dv = 0.0
+    for j in range(wl.world):
+        pos = shares[j].q_positions
+        err_dk = max(err_dk, _rel_err(dk[j].cpu().numpy(), full_dk[:, :, pos]))
+        err_dv = max(err_dv, _rel_err(dv[j].cpu().numpy(), full_dv[:, :, pos]))
+    print(f"  {name}: rel err dQ={err_dq:.3e} dK={err_dk:.3e} dV={err_dv:.3e}", flush=True)
+    assert err_dq <= TOL_REL and err_dk <= TOL_REL and err_dv <= TOL_REL
+
+
+def test_step_loop_matches_driver_bitwise(gpu):
+    """ring_attn_backward_step over the ring order, by hand, equals the driver."""
+    import torch
+    wl = BW["bwd_zigzag4k_4dev_gqa"]
+    dev = torch.device("cuda:0")
+    share = harness.build_share(wl, 1, dev)
+    out, lse = harness.run_forward(share, copy_stream=_copy_stream())
+    d_out = harness.build_upstream(share)
+    dk_a, dv_a = harness.new_kv_grads(share)
+    dq_a = harness.run_backward(share, out, lse, d_out, dk_a, dv_a, copy_stream=_copy_stream())
+
+    rd = share.ring_desc()
+    sd0, _ = ra.ring_step_desc(rd, 0)
+    terms = torch.empty((2, wl.batch, wl.heads_q, wl.local_len), dtype=torch.float32, device=dev)
+    ra.backward_prep(sd0, out, d_out, lse, terms)
+    dq = torch.empty(share.q.shape, dtype=torch.float32, device=dev)
+    dk_b, dv_b = harness.new_kv_grads(share)
+    first = True
+    for s in range(wl.world):
+        sd, owner = ra.ring_step_desc(rd, s)
+        if ra.visible_pairs(sd) == 0:
+            continue
+        ra.backward_step(sd, share.q, share.k_blocks[owner], share.v_blocks[owner], d_out, terms, dq,
+                         dk_b[owner], dv_b[owner], init_dq=first)
+        first = False
+    torch.cuda.synchronize()
+    assert torch.equal(dq.to(torch.bfloat16), dq_a)
+    for j in range(wl.world):
+        assert torch.equal(dk_a[j], dk_b[j]) and torch.equal(dv_a[j], dv_b[j])
+
+
+def test_backward_is_deterministic_and_accumulates(gpu):
+    """Two runs give identical bits; running a device twice doubles its dK/dV."""
+    import torch
+    wl = BW["bwd_striped2k_2dev_b2"]
+    dev = torch.device("cuda:0")
+    share = harness.build_share(wl, 0, dev)
+    out, lse = harness.run_forward(share, copy_stream=_copy_stream())
+    d_out = harness.build_upstream(share)
+    dk1, dv1 = harness.new_kv_grads(share)
+    dk2, dv2 = harness.new_kv_grads(share)
+    dq1 = harness.run_backward(share, out, lse, d_out, dk1, dv1, copy_stream=_copy_stream())
+    dq2 = harness.run_backward(share, out, lse, d_out, dk2, dv2, copy_stream=_copy_stream())
+    harness.run_backward(share, out, lse, d_out, dk2, dv2, copy_stream=_copy_stream())
+    torch.cuda.synchronize()
+    assert torch.equal(dq1, dq2)
+    for j in range(wl.world):
+        assert torch.equal(2 * dk1[j], dk2[j]) and torch.equal(2 * dv1[j], dv2[j])
+
+
+def test_full_size_backward_sampled_rows_and_identities(gpu):
+    import torch
+    wl = ring_inputs.WORKLOADS["zigzag128k_8dev_gqa"]
+    dev = torch.device("cuda:0")
+    share = harness.build_share(wl, 0, dev)
+    cs = _copy_stream()
+    out, lse = harness.run_forward(share, copy_stream=cs)
+    d_out = harness.build_upstream(share)
+    dk, dv = harness.new_kv_grads(share)
+    dq = harness.run_backward(share, out, lse, d_out, dk, dv, copy_stream=cs)
+    torch.cuda.synchronize()
+
+    # dQ rows: each depends on its own row only
+    c = wl.local_len
+    rng = np.random.default_rng(17)
+    rows = sorted({0, 1, 255, 256, c // 2 - 1, c // 2, c - 1} | set(rng.choice(c, 40, replace=False).tolist()))
+    pos = share.q_positions[rows]
+    k_pos = np.arange(wl.total_len)
+    dq_np = dq[:, :, rows].float().cpu().numpy()
+    scale = 1.0 / np.sqrt(wl.head_dim)
+    err = 0.0
+    group = wl.heads_q // wl.heads_kv
+    for g in range(wl.heads_kv):
+        k = ring_inputs.head(wl, "k", 0, g)
+        v = ring_inputs.head(wl, "v", 0, g)
+        for h in range(g * group, (g + 1) * group):
+            q = ring_inputs.rows(wl, "q", 0, h, pos)
+            do = ring_inputs.rows(wl, "do", 0, h, pos)
+            r = oracle.attention_backward_rows(q, pos, k, v, k_pos, do, True)
+            a = (np.abs(do.astype(np.float64)) * np.abs(r["out"])).sum(axis=1, keepdims=True)
+            budget = (scale * (2.0 ** -7 * a * np.abs(r["p_k"]) + 2.0 ** -8 * r["abs_ds_k"]) +
+                      2.0 ** -8 * np.abs(r["dq"]) + 1e-4)
+            assert np.isfinite(dq_np[0, h]).all()
+            err = max(err, float((np.abs(dq_np[0, h] - r["dq"]) / budget).max()))
+    # Identities of one device's contribution, per KV head and column. Every
+    # row's P~ sums to 1 within 2^-8 (LSE within 1e-3, bf16 rounding 2^-9),
+    # so |sum dV - sum dO| <= 2^-8 sum |dO|; the dS~ of a row sum to D - D~,
+    # far below 1 % of sum |dK| here.
+    sum_dk = sum(x.double().sum(dim=2) for x in dk)          # [B, Hkv, d]
+    sum_dv = sum(x.double().sum(dim=2) for x in dv)
+    abs_dk = sum(x.double().abs().sum(dim=2) for x in dk)
+    grouped = d_out.double().reshape(wl.batch, wl.heads_kv, group, wl.local_len, wl.head_dim)
+    do_sum = grouped.sum(dim=(2, 3))
+    do_abs = grouped.abs().sum(dim=(2, 3))
+    id_dk = float((sum_dk.abs() / abs_dk).max())
+    id_dv = float(((sum_dv - do_sum).abs() / do_abs).max())
+    print(f"  dQ rows={len(rows)} x {wl.heads_q} heads: max err / budget {err:.3f}; "
+          f"|sum dK|/sum|dK| {id_dk:.3e}; |sum dV - sum dO|/sum|dO| {id_dv:.3e}", flush=True)
+    assert err <= 1.0
+    assert id_dk <= 1e-2 and id_dv <= 2.0 ** -8

@@ -104,6 +104,23 @@ def test_invariants_of_softmax_attention():
     np.testing.assert_allclose(r["delta"], (p * dp).sum(axis=1), atol=1e-10)
 
 
+def test_error_terms():
+    """p_k is attention with the keys as values; |dQ| <= scale * abs_ds_k
+    (triangle inequality), with equality where every dS_ij k_j has one sign."""
+    rng = np.random.default_rng(16)
+    q, k, v, do, q_pos, k_pos = _case(rng, 16, 40, 8, True)
+    r = oracle.attention_backward_rows(q, q_pos, k, v, k_pos, do, True)
+    o_k, _ = oracle.attention_rows(q, q_pos, k, k, k_pos, True)
+    np.testing.assert_allclose(r["p_k"], o_k, atol=1e-12)
+    scale = 1 / math.sqrt(8)
+    assert (np.abs(r["dq"]) <= scale * r["abs_ds_k"] + 1e-12).all()
+    kp = np.abs(k)
+    r2 = oracle.attention_backward_rows(q[:1], [39], kp, v, k_pos, do[:1], True)
+    # one row, keys all positive: |sum_j dS_j k_j| < sum_j |dS_j| k_j unless dS has one sign (it never
+    # does: the dS of a row sum to zero), so the bound is strict here
+    assert (np.abs(r2["dq"]) < scale * r2["abs_ds_k"]).all()
+
+
 def test_single_visible_key():
     """A causal row at position 0 sees only key 0: O_0 = v_0, so its dQ is
     zero, it adds dO_0 to dV_0 and nothing to dK."""
