@@ -38,6 +38,15 @@ using namespace bf16k;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+#ifndef RA_BWD_SCHED
+#define RA_BWD_SCHED 0
+#endif
+#ifndef RA_BWD_AHEAD
+#define RA_BWD_AHEAD 8
+#endif
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedTrans = 0x400;
+
 constexpr int kD = 128;
 constexpr int kRowB = kD * 2;      // one bf16 row
 constexpr int kTileB = 64 * kRowB;  // 64 rows: 16 KB
@@ -82,6 +91,27 @@ __device__ __forceinline__ void copy_tile_blocks(const i32x4& rsrc, uint32_t dst
     const int r = u >> 4;
     const int p = u & 15;
     dma16(rsrc, dst + blk * 1024, r * kRowB + ((p ^ bswz(r)) << 4));
+  }
+}
+
+// Scheduling shape of N MFMAs that take R LDS reads each, interleaved with
+// vector work: the reads run AHEAD MFMAs ahead of their use, and V vector
+// instructions and T transcendental ones follow every MFMA.
+template <int N, int R, int AHEAD, int V, int T>
+__device__ __forceinline__ void sched_mfma_reads_valu() {
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, AHEAD * R, 0);
+#pragma unroll
+  for (int i = 0; i < N - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, R, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedValu, V, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedTrans, T, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedValu, V, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedTrans, T, 0);
   }
 }
 
@@ -266,7 +296,7 @@ __global__ void __launch_bounds__(kQWaves * 64) bwd_dq_kernel(BwdArgs a, int32_t
 // ============================================================================
 constexpr int kKWaves = 4;
 constexpr int kKKeys = kKWaves * 32;
-constexpr int kKStages = 3;
+constexpr int kKStages = 4;
 constexpr int kKOffDo = kTileB;
 constexpr int kKOffC = 2 * kTileB;         // 64 row terms c (1 KB region: the copy writes 64 lanes x 16 B)
 constexpr int kKOffE = 2 * kTileB + 1024;  // 64 row terms e
@@ -400,8 +430,15 @@ bwd_dkdv_kernel(BwdArgs a, int32_t k_tiles) {
       dva[db][j] = 0.0f;
     }
 
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  for (int it = 0; it < total; ++it) {
+  // Tile `it` is published at the start of iteration it. Its S and dP
+  // products run first; then the dV/dK products of tile it-1 (which need only
+  // its packed P and dS and its LDS stage) are interleaved with the vector
+  // work (mask, P, dS) of tile it, so the matrix cores keep busy while the
+  // wave exponentiates. With four stages and copies issued two tiles ahead,
+  // the stage refilled at iteration it held tile it-2, last read in
+  // iteration it-1, before this iteration's barrier.
+  bf16x8 pf[2][2], dsf[2][2];
+  auto publish = [&](int it) {
     // Waves 0 and 1 also copy one block of row terms per tile.
     if (it + 1 < total) {
       if (wave < 2)
@@ -413,14 +450,11 @@ bwd_dkdv_kernel(BwdArgs a, int32_t k_tiles) {
     }
     asm volatile("s_barrier" ::: "memory");
     if (it + 2 < total) issue(it + 2);
+  };
+  // S = Q K^T and dP = dO V^T, accumulators started at the row terms
+  // (S - LSE/scale and dP - D); then the causal mask of partial tiles.
+  auto products = [&](int it, f32x16 (&sacc)[2], f32x16 (&pacc)[2]) {
     const uint32_t so = (uint32_t)(it % kKStages) * kKStageB;
-    int32_t h;
-    const RowRange* r;
-    int64_t rs;
-    decode(it, &h, &r, &rs);
-
-    // Accumulators start at the row terms: S - LSE/scale and dP - D.
-    f32x16 sacc[2], pacc[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -428,14 +462,11 @@ bwd_dkdv_kernel(BwdArgs a, int32_t k_tiles) {
         const uint32_t ro = (uint32_t)((32 * rb + 8 * jj + 4 * hh) * 4);
         const f32x4 c4 = *lds_ptr<f32x4>(smem_base + so + kKOffC + ro);
         const f32x4 e4 = *lds_ptr<f32x4>(smem_base + so + kKOffE + ro);
-        sacc[rb][4 * jj + 0] = c4.x;
-        sacc[rb][4 * jj + 1] = c4.y;
-        sacc[rb][4 * jj + 2] = c4.z;
-        sacc[rb][4 * jj + 3] = c4.w;
-        pacc[rb][4 * jj + 0] = e4.x;
-        pacc[rb][4 * jj + 1] = e4.y;
-        pacc[rb][4 * jj + 2] = e4.z;
-        pacc[rb][4 * jj + 3] = e4.w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sacc[rb][4 * jj + i] = c4[i];
+          pacc[rb][4 * jj + i] = e4[i];
+        }
       }
 #pragma unroll
     for (int c = 0; c < 8; ++c)
@@ -446,18 +477,29 @@ bwd_dkdv_kernel(BwdArgs a, int32_t k_tiles) {
         sacc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[c], sacc[rb], 0, 0, 0);
         pacc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[c], pacc[rb], 0, 0, 0);
       }
-
+#if RA_BWD_SCHED
+    // the 16 row-term reads first (they start the accumulators), then the
+    // operand reads RA_BWD_AHEAD MFMAs ahead of their use
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 16, 0);
+    sched_mfma_reads_valu<32, 1, RA_BWD_AHEAD, 0, 0>();
+#endif
+    int32_t h;
+    const RowRange* r;
+    int64_t rs;
+    decode(it, &h, &r, &rs);
     if (causal && rs < r->full) {
+      // rows of the tile before this lane's first visible row see no key of it
       const int64_t fv = r == &ra0 ? fv0 : fv1;
+      const int64_t d = fv - rs;
+      const int32_t lim = d < 0 ? 0 : (d > 64 ? 64 : (int32_t)d);
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int64_t qrow = rs + 32 * rb + 8 * (j >> 2) + 4 * hh + (j & 3);
-          if (qrow < fv) sacc[rb][j] = -INFINITY;
-        }
+        for (int j = 0; j < 16; ++j)
+          if (32 * rb + 8 * (j >> 2) + 4 * hh + (j & 3) < lim) sacc[rb][j] = -INFINITY;
     }
-    bf16x8 pf[2][2], dsf[2][2];
+  };
+  auto softmax = [&](f32x16 (&sacc)[2], f32x16 (&pacc)[2]) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
@@ -471,6 +513,10 @@ bwd_dkdv_kernel(BwdArgs a, int32_t k_tiles) {
       dsf[rb][0] = pack_p(pacc[rb], 0);
       dsf[rb][1] = pack_p(pacc[rb], 8);
     }
+  };
+  // dV^T += dO^T P and dK^T += Q^T dS of tile `it` (P, dS given packed).
+  auto grads = [&](int it, const bf16x8 (&p)[2][2], const bf16x8 (&ds)[2][2]) {
+    const uint32_t so = (uint32_t)(it % kKStages) * kKStageB;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
@@ -478,10 +524,37 @@ bwd_dkdv_kernel(BwdArgs a, int32_t k_tiles) {
         const uint32_t off = so + kc * 16 * kRowB;
         const bf16x8 ot = read_tr(lo, hi, db, off + kKOffDo);
         const bf16x8 qt = read_tr(lo, hi, db, off);
-        dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot, pf[kc >> 1][kc & 1], dva[db], 0, 0, 0);
-        dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, dsf[kc >> 1][kc & 1], dka[db], 0, 0, 0);
+        dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot, p[kc >> 1][kc & 1], dva[db], 0, 0, 0);
+        dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, ds[kc >> 1][kc & 1], dka[db], 0, 0, 0);
       }
+  };
+
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  {
+    publish(0);
+    f32x16 sacc[2], pacc[2];
+    products(0, sacc, pacc);
+    softmax(sacc, pacc);
   }
+  for (int it = 1; it < total; ++it) {
+    publish(it);
+    f32x16 sacc[2], pacc[2];
+    products(it, sacc, pacc);
+    bf16x8 pp[2][2], dp[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        pp[i][k] = pf[i][k];
+        dp[i][k] = dsf[i][k];
+      }
+    grads(it - 1, pp, dp);
+    softmax(sacc, pacc);
+#if RA_BWD_SCHED
+    sched_mfma_reads_valu<32, 2, RA_BWD_AHEAD, 3, 1>();
+#endif
+  }
+  grads(total - 1, pf, dsf);
 
   if (!valid) return;
   float* dkp = a.dk + kvrow * kD;
