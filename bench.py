@@ -275,7 +275,7 @@ def bench_backward(wl, rank, K, Wm):
         "metric": "effective causal attention-backward TFLOP/s of one device's ring share at 1 GPU",
         "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": Wm,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": wl.dtype, "data": "synthetic (seeded N(0,1) Q/K/V/dO, bf16-rounded)",
+        "dtype": wl.dtype, "data": "synthetic (seeded Q/K/V as the workload states, dO N(0,1); bf16-rounded)",
         "config": {"workload": wl.name, "pass": "backward", "description": wl.description, "batch": wl.batch,
                    "heads_q": wl.heads_q, "heads_kv": wl.heads_kv, "head_dim": wl.head_dim,
                    "local_len": wl.local_len, "world": wl.world, "rank": rank, "partition": wl.partition},

@@ -234,7 +234,7 @@ int ring_attn_ulysses_forward(const ra_ulysses_desc* desc, const void* const* q_
  * i over the local query rows, j over the keys of one K/V block. dQ stays on
  * the device; dK and dV are accumulators that travel around the ring with
  * their K/V block and are back at the block's owner after a full turn.
- * Built for RA_BF16 with head_dim 128 (other shapes: RA_ERR_UNSUPPORTED). */
+ * Built for RA_BF16 with head_dim 64 or 128 (RA_F32: RA_ERR_UNSUPPORTED). */
 
 #define RA_BWD_INIT_DQ 1          /* ring_attn_backward_step: dq_acc starts at 0 */
 

@@ -682,12 +682,11 @@ float scale_of(const ra_step_desc* d) {
   return d->scale > 0.0f ? d->scale : (float)(1.0 / std::sqrt((double)d->head_dim));
 }
 
-// The backward kernels are built for bf16 with head_dim 128.
+// The backward kernels are built for bf16 (head_dim 64 or 128).
 int check_backward_shape(const ra_step_desc* d) {
   int rc = check_shape(d, true);
   if (rc) return rc;
-  if (d->dtype != RA_BF16 || d->head_dim != 128)
-    return fail(RA_ERR_UNSUPPORTED, "the backward step is built for bf16 with head_dim 128");
+  if (d->dtype != RA_BF16) return fail(RA_ERR_UNSUPPORTED, "the backward step is built for bf16");
   return RA_OK;
 }
 
@@ -784,8 +783,7 @@ int ring_attn_backward(const ra_ring_desc* d, const void* q_local, const void* c
                        void* compute_stream, void* copy_stream, void* const* step_events) {
   int rc = check_ring_desc(d);
   if (rc) return rc;
-  if (d->dtype != RA_BF16 || d->head_dim != 128)
-    return fail(RA_ERR_UNSUPPORTED, "the backward step is built for bf16 with head_dim 128");
+  if (d->dtype != RA_BF16) return fail(RA_ERR_UNSUPPORTED, "the backward step is built for bf16");
   const int n = d->world;
   const bool has_rows = d->local_len > 0 && d->batch > 0;
   if (!k_blocks || !v_blocks || !dk_acc || !dv_acc)

@@ -23,7 +23,7 @@ struct BwdArgs {
 // terms[r] = -lse[r] / scale (or -inf), terms[rows + r] = -(dout[r] . out[r]).
 hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, float* terms, int64_t rows,
                            int head_dim, int dtype, float scale, hipStream_t s);
-// dq += ..., dk += ..., dv += ... for one K/V block (bf16, head_dim 128).
+// dq += ..., dk += ..., dv += ... for one K/V block (bf16, head_dim 64 or 128).
 hipError_t launch_bwd_bf16(const BwdArgs& a, int head_dim, hipStream_t s);
 // y = x converted to dtype (RA_F32 copies), n a multiple of 4.
 hipError_t launch_convert(const float* x, void* y, int64_t n, int dtype, hipStream_t s);

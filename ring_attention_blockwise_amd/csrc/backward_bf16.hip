@@ -1,4 +1,4 @@
-// Backward ring step on the CDNA4 matrix cores (gfx950), bf16, head_dim 128.
+// Backward ring step on the CDNA4 matrix cores (gfx950), bf16, head_dim 64 or 128.
 //
 // The pages run the ring forward only ("distributed training hands-on code",
 // section 6.2, has no backward pass); this is the plain extension of the same
@@ -47,22 +47,36 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kSchedValu = 0x002;
 constexpr int kSchedTrans = 0x400;
 
-constexpr int kD = 128;
-constexpr int kRowB = kD * 2;      // one bf16 row
-constexpr int kTileB = 64 * kRowB;  // 64 rows: 16 KB
-
-__device__ __forceinline__ int bswz(int row) { return 4 * (row & 3) + ((row >> 2) & 3); }
+// Tile geometry for head_dim D (64 or 128): rows of D bf16, 64-row tiles.
+template <int D>
+struct BL {
+  static constexpr int kRowB = D * 2;         // one bf16 row
+  static constexpr int kUnits = D / 8;         // 16-byte units per row
+  static constexpr int kTileB = 64 * kRowB;    // 64 rows
+  static constexpr int kDC = D / 16;           // K=16 chunks of a head_dim contraction
+  static constexpr int kDB = D / 32;           // 32-column blocks of head_dim
+  // Stored unit of logical unit u in row r is u ^ swz(r). D = 128 (16 units,
+  // one row per 256-byte bank window): 4 (r mod 4) + (r / 4 mod 4). D = 64
+  // (8 units, two rows per window): 4 (r / 2 mod 2) + (r / 4 mod 4). Either
+  // way the 16 rows of a row-wise b128 read and the 4 rows x 4 units of a
+  // transposed half-wave read land on distinct banks.
+  __device__ static __forceinline__ int swz(int r) {
+    return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+  }
+};
 
 // Row-wise read (A operand, lane = row qcol of a 32-row block, 8 consecutive
 // elements of logical unit 2c + hh).
+template <int D>
 __device__ __forceinline__ uint32_t row_read_addr(uint32_t base, int qcol, int hh, int c) {
-  return base + qcol * kRowB + (((2 * c + hh) ^ bswz(qcol)) << 4);
+  return base + qcol * BL<D>::kRowB + (((2 * c + hh) ^ BL<D>::swz(qcol)) << 4);
 }
 
 // Transposed read for ds_read_b64_tr_b16: d block db, lower (e = 0) or upper
 // (e = 1) 8-row half of a 16-row chunk. Within a 16-lane group, source lane
 // 4t + q points at row 8e + 4hh + t and columns 32db + 16(group & 1) + 4q..;
 // output lane l then holds column 32db + l % 32 at rows 8e + 4hh + 0..3.
+template <int D>
 __device__ __forceinline__ uint32_t tr_read_addr(uint32_t base, int lane, int db, int e) {
   const int hh = lane >> 5;
   const int grp16 = lane >> 4;
@@ -70,13 +84,14 @@ __device__ __forceinline__ uint32_t tr_read_addr(uint32_t base, int lane, int db
   const int q4 = lane & 3;
   const int row = 8 * e + 4 * hh + t4;
   const int unit = 4 * db + 2 * (grp16 & 1) + (q4 >> 1);
-  return base + row * kRowB + ((unit ^ bswz(row)) << 4) + ((q4 & 1) << 3);
+  return base + row * BL<D>::kRowB + ((unit ^ BL<D>::swz(row)) << 4) + ((q4 & 1) << 3);
 }
 
 // A operand of a product that contracts over the rows of a tile: columns
 // 32db + lane % 32, rows {0-3, 8-11} + 4hh of the 16-row chunk at byte offset
 // `off` — the row order of the B operands packed from accumulators.
-__device__ __forceinline__ bf16x8 read_tr(const uint32_t (&lo)[4], const uint32_t (&hi)[4], int db, uint32_t off) {
+template <int N>
+__device__ __forceinline__ bf16x8 read_tr(const uint32_t (&lo)[N], const uint32_t (&hi)[N], int db, uint32_t off) {
   const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lds_ptr<s16x4>(lo[db] + off));
   const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lds_ptr<s16x4>(hi[db] + off));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -84,13 +99,14 @@ __device__ __forceinline__ bf16x8 read_tr(const uint32_t (&lo)[4], const uint32_
 
 // Copy `nb` 1 KB blocks of a 64-row tile (rows [0, nrows) of `src` valid,
 // the rest read as zero) into LDS at dst, blocks first_block .. +nb.
+template <int D>
 __device__ __forceinline__ void copy_tile_blocks(const i32x4& rsrc, uint32_t dst, int first_block, int nb, int lane) {
   for (int i = 0; i < nb; ++i) {
     const int blk = first_block + i;
     const int u = blk * 64 + lane;
-    const int r = u >> 4;
-    const int p = u & 15;
-    dma16(rsrc, dst + blk * 1024, r * kRowB + ((p ^ bswz(r)) << 4));
+    const int r = u / BL<D>::kUnits;
+    const int p = u % BL<D>::kUnits;
+    dma16(rsrc, dst + blk * 1024, r * BL<D>::kRowB + ((p ^ BL<D>::swz(r)) << 4));
   }
 }
 
@@ -121,10 +137,12 @@ __device__ __forceinline__ void sched_mfma_reads_valu() {
 constexpr int kQWaves = 8;
 constexpr int kQRows = kQWaves * 32;
 constexpr int kQStages = 3;
-constexpr int kQStageB = 2 * kTileB;                    // K tile, then V tile
-constexpr int kQCopies = 2 * (kTileB / 1024) / kQWaves;  // 1 KB copies per wave per tile
-
+template <int D>
 __global__ void __launch_bounds__(kQWaves * 64) bwd_dq_kernel(BwdArgs a, int32_t q_tiles) {
+  using L = BL<D>;
+  constexpr int kD = D, kRowB = L::kRowB, kTileB = L::kTileB, kDC = L::kDC, kDB = L::kDB;
+  constexpr int kQStageB = 2 * kTileB;                    // K tile, then V tile
+  constexpr int kQCopies = 2 * (kTileB / 1024) / kQWaves;  // 1 KB copies per wave per tile
   __shared__ __attribute__((aligned(1024))) char smem[kQStages * kQStageB];
   const StepArgs& s = a.s;
   const int32_t n_bh = s.batch * s.heads_q;
@@ -168,19 +186,19 @@ __global__ void __launch_bounds__(kQWaves * 64) bwd_dq_kernel(BwdArgs a, int32_t
     const uint32_t dst = smem_base + (uint32_t)(t % kQStages) * kQStageB;
     const i32x4 rk = buffer_resource(kg + (int64_t)start * kRowB, nbytes);
     const i32x4 rv = buffer_resource(vg + (int64_t)start * kRowB, nbytes);
-    copy_tile_blocks(rk, dst, wave * (kQCopies / 2), kQCopies / 2, lane);
-    copy_tile_blocks(rv, dst + kTileB, wave * (kQCopies / 2), kQCopies / 2, lane);
+    copy_tile_blocks<D>(rk, dst, wave * (kQCopies / 2), kQCopies / 2, lane);
+    copy_tile_blocks<D>(rv, dst + kTileB, wave * (kQCopies / 2), kQCopies / 2, lane);
   };
   if (ntiles > 0) issue(0);
   if (ntiles > 1) issue(1);
 
   // Q^T and dO^T fragments (B operands): row rowc, elements 16c + 8hh .. +7.
-  bf16x8 qf[8], of[8];
+  bf16x8 qf[kDC], of[kDC];
   {
     const bf16x8* qp = reinterpret_cast<const bf16x8*>(static_cast<const unsigned short*>(s.q) + srow * kD);
     const bf16x8* op = reinterpret_cast<const bf16x8*>(static_cast<const unsigned short*>(a.dout) + srow * kD);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int c = 0; c < kDC; ++c) {
       qf[c] = qp[2 * c + hh];
       of[c] = op[2 * c + hh];
     }
@@ -192,19 +210,19 @@ __global__ void __launch_bounds__(kQWaves * 64) bwd_dq_kernel(BwdArgs a, int32_t
   const int32_t vend0 = row_visible_end(s, plan.r0, qpos);
   const int32_t vend1 = row_visible_end(s, plan.r1, qpos);
 
-  uint32_t k_addr[8];
+  uint32_t k_addr[kDC];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) k_addr[c] = row_read_addr(smem_base, qcol, hh, c);
-  uint32_t lo[4], hi[4];
+  for (int c = 0; c < kDC; ++c) k_addr[c] = row_read_addr<D>(smem_base, qcol, hh, c);
+  uint32_t lo[kDB], hi[kDB];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    lo[db] = tr_read_addr(smem_base, lane, db, 0);
-    hi[db] = tr_read_addr(smem_base, lane, db, 1);
+  for (int db = 0; db < kDB; ++db) {
+    lo[db] = tr_read_addr<D>(smem_base, lane, db, 0);
+    hi[db] = tr_read_addr<D>(smem_base, lane, db, 1);
   }
 
-  f32x16 dqa[4];
+  f32x16 dqa[kDB];
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < kDB; ++db)
 #pragma unroll
     for (int j = 0; j < 16; ++j) dqa[db][j] = 0.0f;
 
@@ -230,7 +248,7 @@ __global__ void __launch_bounds__(kQWaves * 64) bwd_dq_kernel(BwdArgs a, int32_t
         pacc[kb][j] = 0.0f;
       }
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
+    for (int c = 0; c < kDC; ++c)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const bf16x8 kf = *lds_ptr<bf16x8>(k_addr[c] + so + kb * 32 * kRowB);
@@ -265,7 +283,7 @@ __global__ void __launch_bounds__(kQWaves * 64) bwd_dq_kernel(BwdArgs a, int32_t
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
+      for (int db = 0; db < kDB; ++db) {
         const bf16x8 kt = read_tr(lo, hi, db, so + kc * 16 * kRowB);
         dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsf[kc >> 1][kc & 1], dqa[db], 0, 0, 0);
       }
@@ -274,7 +292,7 @@ __global__ void __launch_bounds__(kQWaves * 64) bwd_dq_kernel(BwdArgs a, int32_t
   if (!valid) return;
   float* dst = a.dq + srow * kD;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < kDB; ++db)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       float4* p = reinterpret_cast<float4*>(dst + 32 * db + 8 * jj + 4 * hh);
@@ -297,11 +315,6 @@ __global__ void __launch_bounds__(kQWaves * 64) bwd_dq_kernel(BwdArgs a, int32_t
 constexpr int kKWaves = 4;
 constexpr int kKKeys = kKWaves * 32;
 constexpr int kKStages = 4;
-constexpr int kKOffDo = kTileB;
-constexpr int kKOffC = 2 * kTileB;         // 64 row terms c (1 KB region: the copy writes 64 lanes x 16 B)
-constexpr int kKOffE = 2 * kTileB + 1024;  // 64 row terms e
-constexpr int kKStageB = 2 * kTileB + 2048;
-constexpr int kKCopies = (kTileB / 1024) / kKWaves;  // per tensor, per wave
 
 // Query rows [begin, end) of one query segment that see a key of the tile;
 // rows from `full` on see every key of it.
@@ -329,8 +342,18 @@ __device__ __forceinline__ RowRange row_range(const StepArgs& s, int seg, int64_
   return r;
 }
 
+template <int D>
 __global__ void __launch_bounds__(kKWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 bwd_dkdv_kernel(BwdArgs a, int32_t k_tiles) {
+  using L = BL<D>;
+  constexpr int kD = D, kRowB = L::kRowB, kTileB = L::kTileB, kDC = L::kDC, kDB = L::kDB;
+  // stage: Q tile, dO tile, 64 row terms c, 64 row terms e (1 KB regions:
+  // their copies write 64 lanes x 16 B)
+  constexpr int kKOffDo = kTileB;
+  constexpr int kKOffC = 2 * kTileB;
+  constexpr int kKOffE = 2 * kTileB + 1024;
+  constexpr int kKStageB = 2 * kTileB + 2048;
+  constexpr int kKCopies = (kTileB / 1024) / kKWaves;  // per tensor, per wave
   __shared__ __attribute__((aligned(1024))) char smem[kKStages * kKStageB];
   const StepArgs& s = a.s;
   const int32_t n_bk = s.batch * s.heads_kv;
@@ -363,12 +386,12 @@ bwd_dkdv_kernel(BwdArgs a, int32_t k_tiles) {
   const size_t kvrow = (size_t)(((int64_t)b * s.heads_kv + kvh) * s.kv_len + keyc);
 
   // K^T and V^T fragments (B operands): key keyc, elements 16c + 8hh .. +7.
-  bf16x8 kf[8], vf[8];
+  bf16x8 kf[kDC], vf[kDC];
   {
     const bf16x8* kp = reinterpret_cast<const bf16x8*>(static_cast<const unsigned short*>(s.k) + kvrow * kD);
     const bf16x8* vp = reinterpret_cast<const bf16x8*>(static_cast<const unsigned short*>(s.v) + kvrow * kD);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int c = 0; c < kDC; ++c) {
       kf[c] = kp[2 * c + hh];
       vf[c] = vp[2 * c + hh];
     }
@@ -402,28 +425,28 @@ bwd_dkdv_kernel(BwdArgs a, int32_t k_tiles) {
     const uint32_t dst = smem_base + (uint32_t)(it % kKStages) * kKStageB;
     const i32x4 rq = buffer_resource(static_cast<const unsigned short*>(s.q) + first * kD, nrows * kRowB);
     const i32x4 ro = buffer_resource(static_cast<const unsigned short*>(a.dout) + first * kD, nrows * kRowB);
-    copy_tile_blocks(rq, dst, wave * kKCopies, kKCopies, lane);
-    copy_tile_blocks(ro, dst + kKOffDo, wave * kKCopies, kKCopies, lane);
+    copy_tile_blocks<D>(rq, dst, wave * kKCopies, kKCopies, lane);
+    copy_tile_blocks<D>(ro, dst + kKOffDo, wave * kKCopies, kKCopies, lane);
     if (wave == 0) dma16(buffer_resource(a.terms + first, nrows * 4), dst + kKOffC, lane * 16);
     if (wave == 1) dma16(buffer_resource(a.terms + n_rows + first, nrows * 4), dst + kKOffE, lane * 16);
   };
   issue(0);
   if (total > 1) issue(1);
 
-  uint32_t q_addr[8];
+  uint32_t q_addr[kDC];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) q_addr[c] = row_read_addr(smem_base, qcol, hh, c);
-  uint32_t lo[4], hi[4];
+  for (int c = 0; c < kDC; ++c) q_addr[c] = row_read_addr<D>(smem_base, qcol, hh, c);
+  uint32_t lo[kDB], hi[kDB];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    lo[db] = tr_read_addr(smem_base, lane, db, 0);
-    hi[db] = tr_read_addr(smem_base, lane, db, 1);
+  for (int db = 0; db < kDB; ++db) {
+    lo[db] = tr_read_addr<D>(smem_base, lane, db, 0);
+    hi[db] = tr_read_addr<D>(smem_base, lane, db, 1);
   }
   const float sl2 = s.scale_log2;
 
-  f32x16 dka[4], dva[4];
+  f32x16 dka[kDB], dva[kDB];
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < kDB; ++db)
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       dka[db][j] = 0.0f;
@@ -469,7 +492,7 @@ bwd_dkdv_kernel(BwdArgs a, int32_t k_tiles) {
         }
       }
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
+    for (int c = 0; c < kDC; ++c)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         const bf16x8 qa = *lds_ptr<bf16x8>(q_addr[c] + so + rb * 32 * kRowB);
@@ -520,7 +543,7 @@ bwd_dkdv_kernel(BwdArgs a, int32_t k_tiles) {
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
+      for (int db = 0; db < kDB; ++db) {
         const uint32_t off = so + kc * 16 * kRowB;
         const bf16x8 ot = read_tr(lo, hi, db, off + kKOffDo);
         const bf16x8 qt = read_tr(lo, hi, db, off);
@@ -560,7 +583,7 @@ bwd_dkdv_kernel(BwdArgs a, int32_t k_tiles) {
   float* dkp = a.dk + kvrow * kD;
   float* dvp = a.dv + kvrow * kD;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < kDB; ++db)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int d = 32 * db + 8 * jj + 4 * hh;
@@ -656,18 +679,23 @@ hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, 
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_bf16(const BwdArgs& a, int head_dim, hipStream_t s) {
-  if (head_dim != kD) return hipErrorInvalidValue;
-  if (a.s.q_len == 0 || a.s.batch == 0) return hipSuccess;
+template <int D>
+hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   const int32_t q_tiles = (int32_t)((a.s.q_len + kQRows - 1) / kQRows);
   const int64_t nq = (int64_t)q_tiles * a.s.batch * a.s.heads_q;
-  bwd_dq_kernel<<<dim3((unsigned)nq), kQWaves * 64, 0, s>>>(a, q_tiles);
+  bwd_dq_kernel<D><<<dim3((unsigned)nq), kQWaves * 64, 0, s>>>(a, q_tiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.s.kv_len == 0) return e;
   const int32_t k_tiles = (int32_t)((a.s.kv_len + kKKeys - 1) / kKKeys);
   const int64_t nk = (int64_t)k_tiles * a.s.batch * a.s.heads_kv;
-  bwd_dkdv_kernel<<<dim3((unsigned)nk), kKWaves * 64, 0, s>>>(a, k_tiles);
+  bwd_dkdv_kernel<D><<<dim3((unsigned)nk), kKWaves * 64, 0, s>>>(a, k_tiles);
   return hipGetLastError();
+}
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, int head_dim, hipStream_t s) {
+  if (head_dim != 64 && head_dim != 128) return hipErrorInvalidValue;
+  if (a.s.q_len == 0 || a.s.batch == 0) return hipSuccess;
+  return head_dim == 128 ? launch_bwd_d<128>(a, s) : launch_bwd_d<64>(a, s);
 }
 
 hipError_t launch_convert(const float* x, void* y, int64_t n, int dtype, hipStream_t s) {
