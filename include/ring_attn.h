@@ -234,7 +234,8 @@ int ring_attn_ulysses_forward(const ra_ulysses_desc* desc, const void* const* q_
  * i over the local query rows, j over the keys of one K/V block. dQ stays on
  * the device; dK and dV are accumulators that travel around the ring with
  * their K/V block and are back at the block's owner after a full turn.
- * Built for RA_BF16 with head_dim 64 or 128 (RA_F32: RA_ERR_UNSUPPORTED). */
+ * Built for head_dim 64 and 128: bf16 on the matrix cores, fp32 on the vector
+ * ALUs (fp32 arithmetic throughout). */
 
 #define RA_BWD_INIT_DQ 1          /* ring_attn_backward_step: dq_acc starts at 0 */
 
@@ -251,9 +252,9 @@ int ring_attn_backward_prep(const ra_step_desc* desc, const void* out, const voi
 
 /* One backward step: the gradient contributions of the local query rows
  * against one K/V block (same descriptor as the forward step).
- *   q          [B, Hq,  q_len,  d] bf16    read
- *   k, v       [B, Hkv, kv_len, d] bf16    read
- *   d_out      [B, Hq,  q_len,  d] bf16    read
+ *   q          [B, Hq,  q_len,  d] dtype   read
+ *   k, v       [B, Hkv, kv_len, d] dtype   read
+ *   d_out      [B, Hq,  q_len,  d] dtype   read
  *   terms      as ring_attn_backward_prep wrote them               read
  *   dq_acc     [B, Hq,  q_len,  d] fp32    read (unless RA_BWD_INIT_DQ) and written
  *   dk_acc, dv_acc [B, Hkv, kv_len, d] fp32  read and written (accumulated)

@@ -682,12 +682,10 @@ float scale_of(const ra_step_desc* d) {
   return d->scale > 0.0f ? d->scale : (float)(1.0 / std::sqrt((double)d->head_dim));
 }
 
-// The backward kernels are built for bf16 (head_dim 64 or 128).
-int check_backward_shape(const ra_step_desc* d) {
-  int rc = check_shape(d, true);
-  if (rc) return rc;
-  if (d->dtype != RA_BF16) return fail(RA_ERR_UNSUPPORTED, "the backward step is built for bf16");
-  return RA_OK;
+int check_backward_shape(const ra_step_desc* d) { return check_shape(d, true); }
+
+hipError_t launch_bwd(const ra::BwdArgs& a, int head_dim, int dtype, hipStream_t s) {
+  return dtype == RA_BF16 ? ra::launch_bwd_bf16(a, head_dim, s) : ra::launch_bwd_f32(a, head_dim, s);
 }
 
 struct BwdLayout {
@@ -766,7 +764,7 @@ int ring_attn_backward_step(const ra_step_desc* d, const void* q, const void* k,
   a.dv = dv_acc;
   a.scale = scale_of(d);
   a.init_dq = init;
-  e = ra::launch_bwd_bf16(a, d->head_dim, s);
+  e = launch_bwd(a, d->head_dim, d->dtype, s);
   return e == hipSuccess ? RA_OK : hip_fail(e, "backward step launch");
 }
 
@@ -783,7 +781,6 @@ int ring_attn_backward(const ra_ring_desc* d, const void* q_local, const void* c
                        void* compute_stream, void* copy_stream, void* const* step_events) {
   int rc = check_ring_desc(d);
   if (rc) return rc;
-  if (d->dtype != RA_BF16) return fail(RA_ERR_UNSUPPORTED, "the backward step is built for bf16");
   const int n = d->world;
   const bool has_rows = d->local_len > 0 && d->batch > 0;
   if (!k_blocks || !v_blocks || !dk_acc || !dv_acc)
@@ -882,7 +879,7 @@ int ring_attn_backward(const ra_ring_desc* d, const void* q_local, const void* c
       a.dv = dv_acc[owner[s]];
       a.scale = scale;
       a.init_dq = (s == first);
-      if ((e = ra::launch_bwd_bf16(a, d->head_dim, cs)) != hipSuccess) return hip_fail(e, "backward step launch");
+      if ((e = launch_bwd(a, d->head_dim, d->dtype, cs)) != hipSuccess) return hip_fail(e, "backward step launch");
     }
     if (step_events)
       if ((e = hipEventRecord(static_cast<hipEvent_t>(step_events[2 * s + 1]), cs)) != hipSuccess)
@@ -894,7 +891,8 @@ int ring_attn_backward(const ra_ring_desc* d, const void* q_local, const void* c
   }
   const int64_t n_dq = (int64_t)L.rows * d->head_dim;
   if (first < 0) {
-    if ((e = ra::launch_zero(dq, (size_t)n_dq * 2, cs)) != hipSuccess) return hip_fail(e, "dq clear");
+    if ((e = ra::launch_zero(dq, (size_t)n_dq * (d->dtype == RA_BF16 ? 2 : 4), cs)) != hipSuccess)
+      return hip_fail(e, "dq clear");
     return RA_OK;
   }
   if ((e = ra::launch_convert(dq_acc, dq, n_dq, d->dtype, cs)) != hipSuccess) return hip_fail(e, "dq convert");

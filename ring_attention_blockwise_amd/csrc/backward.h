@@ -25,6 +25,8 @@ hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, 
                            int head_dim, int dtype, float scale, hipStream_t s);
 // dq += ..., dk += ..., dv += ... for one K/V block (bf16, head_dim 64 or 128).
 hipError_t launch_bwd_bf16(const BwdArgs& a, int head_dim, hipStream_t s);
+// The same for fp32 inputs (fp32 arithmetic throughout).
+hipError_t launch_bwd_f32(const BwdArgs& a, int head_dim, hipStream_t s);
 // y = x converted to dtype (RA_F32 copies), n a multiple of 4.
 hipError_t launch_convert(const float* x, void* y, int64_t n, int dtype, hipStream_t s);
 // Zero `bytes` (a multiple of 16) at p with a fill kernel (no memset node

@@ -148,6 +148,10 @@ BACKWARD_WORKLOADS = {
         name="bwd_zigzag2k_4dev_d64", batch=1, heads_q=4, heads_kv=2, head_dim=64, dtype="bf16",
         causal=True, partition="zigzag", world=4, local_len=512, seed=1012, ranks=(0, 1, 2, 3),
         description="backward, causal zigzag, 2048 tokens over 4 devices, 4 Q / 2 KV heads, d64 bf16"),
+    "bwd_f32_zigzag1k_4dev": Workload(
+        name="bwd_f32_zigzag1k_4dev", batch=1, heads_q=4, heads_kv=2, head_dim=128, dtype="f32",
+        causal=True, partition="zigzag", world=4, local_len=256, seed=1013, ranks=(0, 1, 2, 3),
+        description="backward, causal zigzag, 1024 tokens over 4 devices, 4 Q / 2 KV heads, d128 fp32"),
     "bwd_ragged3k_3dev": Workload(
         name="bwd_ragged3k_3dev", batch=1, heads_q=4, heads_kv=1, head_dim=128, dtype="bf16",
         causal=True, partition="zigzag", world=3, local_len=1000, seed=1011, ranks=(0, 1, 2),

@@ -211,8 +211,6 @@ def test_backward_workspace_and_validation():
     nulls = (ctypes.c_void_p * 4)(*([0x10000] * 3 + [None]))
     assert L.ring_attn_backward(ctypes.byref(rd), FAKE, blocks, blocks, FAKE, FAKE, FAKE, FAKE, blocks, nulls,
                                 FAKE, ws, None, None, None) == ra.ERR_INVALID_ARG
-    for bad in (ra.ring_desc(1, 8, 2, 64, 1024, 4, 1, dtype=ra.F32), ra.ring_desc(1, 8, 2, 128, 1024, 4, 1, dtype=ra.F32)):
-        assert L.ring_attn_backward(ctypes.byref(bad), *args, FAKE, 1 << 40, None, None, None) == ra.ERR_UNSUPPORTED
     bad_dim = ra.ring_desc(1, 8, 2, 96, 1024, 4, 1)
     assert L.ring_attn_backward(ctypes.byref(bad_dim), *args, FAKE, 1 << 40, None, None, None) == ra.ERR_UNSUPPORTED
     sd = ra.step_desc(1, 8, 2, 128, 256, 256, causal=False)
@@ -222,8 +220,8 @@ def test_backward_workspace_and_validation():
     mis = ctypes.c_void_p(0x10008)
     assert L.ring_attn_backward_step(ctypes.byref(sd), *step_args[:5], mis, *step_args[6:], 0,
                                      None) == ra.ERR_INVALID_ARG
-    sd32 = ra.step_desc(1, 8, 2, 64, 256, 256, dtype=ra.F32, causal=False)
-    assert L.ring_attn_backward_step(ctypes.byref(sd32), *step_args, 0, None) == ra.ERR_UNSUPPORTED
+    sd96 = ra.step_desc(1, 8, 2, 96, 256, 256, causal=False)
+    assert L.ring_attn_backward_step(ctypes.byref(sd96), *step_args, 0, None) == ra.ERR_UNSUPPORTED
     assert L.ring_attn_backward_prep(ctypes.byref(sd), None, FAKE, FAKE, FAKE, None) == ra.ERR_INVALID_ARG
     causal_no_segments = ra.step_desc(1, 8, 2, 128, 256, 256)
     assert L.ring_attn_backward_step(ctypes.byref(causal_no_segments), *step_args, 0, None) == ra.ERR_INVALID_ARG

@@ -16,7 +16,8 @@ Tolerance (bf16 path): the kernels round P and dS to bf16 (relative error
 2^-9 each) for the matrix products, and the row terms come from the bf16
 forward output (O rounded to bf16, LSE within 1e-3). On the small workloads
 errors are measured as max |GPU - oracle| / max |oracle| per tensor and must
-stay below 2e-2, the forward's output tolerance. On the long rows of the 128K
+stay below 2e-2, the forward's output tolerance (1e-5 for the fp32 path, which
+computes in fp32 throughout, like the fp32 forward's bound). On the long rows of the 128K
 share, D_i = dO_i . O_i computed from the bf16 output can cancel against
 dP_ij (|D_i| up to ~30 next to |dQ_i| ~ 0.01), so dQ is held to a per-element
 budget derived from those two roundings:
@@ -33,7 +34,7 @@ from ring_attention_blockwise_amd import harness
 
 pytestmark = pytest.mark.gpu
 
-TOL_REL = 2e-2
+TOL_REL = {"bf16": 2e-2, "f32": 1e-5}
 BW = ring_inputs.BACKWARD_WORKLOADS
 
 
@@ -67,7 +68,7 @@ def _all_devices(wl):
     return shares, dqs, dk, dv
 
 
-@pytest.mark.parametrize("name", list(BW) + ["zigzag8k_8dev_d128"])
+@pytest.mark.parametrize("name", list(BW) + ["zigzag8k_8dev_d128", "ring4_noncausal_f32"])
 def test_small_backward_every_element(gpu, name):
     wl = BW.get(name) or ring_inputs.WORKLOADS[name]
     shares, dqs, dk, dv = _all_devices(wl)
@@ -84,7 +85,8 @@ def test_small_backward_every_element(gpu, name):
         err_dk = max(err_dk, _rel_err(dk[j].cpu().numpy(), full_dk[:, :, pos]))
         err_dv = max(err_dv, _rel_err(dv[j].cpu().numpy(), full_dv[:, :, pos]))
     print(f"  {name}: rel err dQ={err_dq:.3e} dK={err_dk:.3e} dV={err_dv:.3e}", flush=True)
-    assert err_dq <= TOL_REL and err_dk <= TOL_REL and err_dv <= TOL_REL
+    tol = TOL_REL[wl.dtype]
+    assert err_dq <= tol and err_dk <= tol and err_dv <= tol
 
 
 def test_step_loop_matches_driver_bitwise(gpu):
