@@ -94,9 +94,13 @@ def cpu_baseline(wl, rank, budget_s=12.0):
 KERNEL_SOURCES = ("step_bf16.hip", "bf16_tiles.h", "common.h")
 
 
-def traffic_from_profile(kernel_name, workload_name):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
+BACKWARD_SOURCES = ("backward_bf16.hip", "backward.h", "bf16_tiles.h", "common.h")
+
+
+def traffic_from_profile(kernel_name, workload_name, sources=KERNEL_SOURCES):
+    """HBM bytes per launch (per step for the backward pair) from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source;
+    else None."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"{kernel_name}_{workload_name}_traffic.json")
     if not os.path.exists(path):
@@ -104,7 +108,7 @@ def traffic_from_profile(kernel_name, workload_name):
     with open(path) as f:
         rec = json.load(f)
     digest = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in sources:
         with open(os.path.join(ROOT, "ring_attention_blockwise_amd", "csrc", name), "rb") as f:
             digest.update(f.read())
     if rec.get("source_sha256") != digest.hexdigest():
@@ -284,7 +288,8 @@ def bench_backward(wl, rank, K, Wm):
                          "tflops": round(achieved, 2),
                          "executed_mfma_tflops": round(achieved * 1.4, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_from_profile("backward_bf16", wl.name, BACKWARD_SOURCES)},
     }
     print(json.dumps(rec), flush=True)
 

@@ -145,11 +145,31 @@ __global__ void __launch_bounds__(kQWaves * 64) bwd_dq_kernel(BwdArgs a, int32_t
   constexpr int kQCopies = 2 * (kTileB / 1024) / kQWaves;  // 1 KB copies per wave per tile
   __shared__ __attribute__((aligned(1024))) char smem[kQStages * kQStageB];
   const StepArgs& s = a.s;
-  const int32_t n_bh = s.batch * s.heads_q;
-  const int32_t item = (int32_t)blockIdx.x;
-  const int32_t tile = q_tiles - 1 - item / n_bh;  // heavy (late) causal tiles first
-  const int32_t b = (item % n_bh) / s.heads_q;
-  const int32_t h = (item % n_bh) % s.heads_q;
+  // Workgroup i runs on XCD i % 8. When the (batch, KV head) pairs divide
+  // evenly over the 8 XCDs, each XCD takes whole KV heads, so its L2 holds
+  // the K/V their query tiles stream; heavy (late) causal tiles first.
+  // Otherwise the heavy-first order is dealt round-robin over the XCDs.
+  int32_t tile, b, h;
+  {
+    const int32_t n_items = q_tiles * s.batch * s.heads_q;
+    const int32_t n_bk = s.batch * s.heads_kv;
+    if (n_bk % 8 == 0) {
+      const int32_t per_xcd = n_items / 8;
+      const int32_t item = (int32_t)(blockIdx.x % 8) * per_xcd + (int32_t)(blockIdx.x / 8);
+      const int32_t per_kv = q_tiles * s.group;
+      const int32_t bk = item / per_kv;
+      const int32_t rem = item % per_kv;
+      tile = q_tiles - 1 - rem / s.group;
+      b = bk / s.heads_kv;
+      h = (bk % s.heads_kv) * s.group + rem % s.group;
+    } else {
+      const int32_t n_bh = s.batch * s.heads_q;
+      const int32_t item = (int32_t)blockIdx.x;
+      tile = q_tiles - 1 - item / n_bh;
+      b = (item % n_bh) / s.heads_q;
+      h = (item % n_bh) % s.heads_q;
+    }
+  }
   const int32_t kvh = h / s.group;
 
   const int tid = threadIdx.x;
