@@ -190,3 +190,75 @@ def test_full_size_backward_sampled_rows_and_identities(gpu, name, rank):
           f"|sum dK|/sum|dK| {id_dk:.3e}; |sum dV - sum dO|/sum|dO| {id_dv:.3e}", flush=True)
     assert err <= 1.0
     assert id_dk <= 1e-2 and id_dv <= 2.0 ** -8
+
+
+def _bwd_tensors(sd, dev, seed=5):
+    import torch
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    B, Hq, Hk, D = sd.batch, sd.heads_q, sd.heads_kv, sd.head_dim
+    dt = torch.bfloat16 if sd.dtype == ra.BF16 else torch.float32
+    mk = lambda *shape: torch.randn(*shape, generator=g).to(dev).to(dt)
+    q, d_out = mk(B, Hq, sd.q_len, D), mk(B, Hq, sd.q_len, D)
+    k, v = mk(B, Hk, sd.kv_len, D), mk(B, Hk, sd.kv_len, D)
+    terms = torch.zeros((2, B, Hq, sd.q_len), dtype=torch.float32, device=dev)
+    terms[0] = -8.0 / (sd.head_dim ** -0.5)  # LSE = 8 for every row
+    return q, k, v, d_out, terms
+
+
+def test_backward_step_edge_cases(gpu):
+    """Empty shapes do nothing; a block that no row sees leaves dQ untouched
+    (zeroes it with RA_BWD_INIT_DQ) and dK/dV untouched."""
+    import torch
+    dev = torch.device("cuda:0")
+    f = torch.float32
+    for dims in ((1, 4, 2, 128, 0, 64), (1, 4, 2, 128, 64, 0), (0, 4, 2, 128, 64, 64)):
+        B, Hq, Hk, D, nq, nk = dims
+        sd = ra.step_desc(B, Hq, Hk, D, nq, nk, causal=False)
+        q, k, v, d_out, terms = _bwd_tensors(sd, dev)
+        dq = torch.full((B, Hq, nq, D), 3.0, dtype=f, device=dev)
+        dk = torch.full((B, Hk, nk, D), 5.0, dtype=f, device=dev)
+        dv = torch.full((B, Hk, nk, D), 7.0, dtype=f, device=dev)
+        ra.backward_step(sd, q, k, v, d_out, terms, dq, dk, dv, init_dq=False)
+        torch.cuda.synchronize()
+        assert bool((dq == 3.0).all()) and bool((dk == 5.0).all()) and bool((dv == 7.0).all())
+    # causal: queries at positions 0..99, keys at 500..563 -> no visible pair
+    sd = ra.step_desc(1, 4, 2, 128, 100, 64, q_segs=[(0, 100)], kv_segs=[(500, 64)])
+    q, k, v, d_out, terms = _bwd_tensors(sd, dev)
+    for init in (False, True):
+        dq = torch.full((1, 4, 100, 128), 3.0, dtype=f, device=dev)
+        dk = torch.full((1, 2, 64, 128), 5.0, dtype=f, device=dev)
+        dv = torch.full((1, 2, 64, 128), 7.0, dtype=f, device=dev)
+        ra.backward_step(sd, q, k, v, d_out, terms, dq, dk, dv, init_dq=init)
+        torch.cuda.synchronize()
+        assert bool((dq == (0.0 if init else 3.0)).all())
+        assert bool((dk == 5.0).all()) and bool((dv == 7.0).all())
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rows_without_keys_contribute_nothing(gpu, dtype):
+    """A row whose forward saw no key (LSE = -inf, row term c = -inf) gets
+    dQ = 0 and adds nothing to dK/dV: the result equals the same step with
+    that row's dO set to zero."""
+    import torch
+    dev = torch.device("cuda:0")
+    code = ra.BF16 if dtype == "bf16" else ra.F32
+    sd = ra.step_desc(1, 2, 1, 128, 300, 200, dtype=code, q_segs=[(100, 300)], kv_segs=[(0, 200)])
+    q, k, v, d_out, terms = _bwd_tensors(sd, dev)
+    dead = [0, 17, 255, 299]
+    t1 = terms.clone()
+    t1[0, :, :, dead] = float("-inf")
+    t1[1, :, :, dead] = 0.0
+    d0 = d_out.clone()
+    d0[:, :, dead] = 0
+    f = torch.float32
+    out = []
+    for dd, tt in ((d_out, t1), (d0, t1)):
+        dq = torch.empty((1, 2, 300, 128), dtype=f, device=dev)
+        dk = torch.zeros((1, 1, 200, 128), dtype=f, device=dev)
+        dv = torch.zeros((1, 1, 200, 128), dtype=f, device=dev)
+        ra.backward_step(sd, q, k, v, dd, tt, dq, dk, dv, init_dq=True)
+        out.append((dq, dk, dv))
+    torch.cuda.synchronize()
+    (dq_a, dk_a, dv_a), (dq_b, dk_b, dv_b) = out
+    assert bool(torch.isfinite(dq_a).all()) and bool((dq_a[:, :, dead] == 0).all())
+    assert torch.equal(dq_a, dq_b) and torch.equal(dk_a, dk_b) and torch.equal(dv_a, dv_b)
