@@ -92,6 +92,10 @@ WORKLOADS = {
         name="zigzag128k_8dev_gqa", batch=1, heads_q=32, heads_kv=8, head_dim=128, dtype="bf16",
         causal=True, partition="zigzag", world=8, local_len=16384, seed=1003, ranks=(0,),
         description="one device of a 128K causal context over 8 devices, 32 Q / 8 KV heads, d128 bf16, zigzag"),
+    "striped128k_8dev_gqa": Workload(
+        name="striped128k_8dev_gqa", batch=1, heads_q=32, heads_kv=8, head_dim=128, dtype="bf16",
+        causal=True, partition="striped", world=8, local_len=16384, seed=1003, ranks=(0,),
+        description="the 128K/8 GQA tensors under the striped partition (token t on device t mod 8)"),
     "zigzag1m_64dev": Workload(
         name="zigzag1m_64dev", batch=1, heads_q=8, heads_kv=8, head_dim=128, dtype="bf16",
         causal=True, partition="zigzag", world=64, local_len=16384, seed=1004, ranks=(0,),

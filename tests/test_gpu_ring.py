@@ -199,3 +199,18 @@ def test_full_size_workload_sampled_rows(gpu, name, rank):
     assert torch.isfinite(out.float()).all()
     if wl.v_dist == "uniform":
         assert out.float().abs().max().item() <= 1.0
+
+
+@pytest.mark.parametrize("rank", [0, 5])
+def test_full_size_striped_partition_sampled_rows(gpu, rank):
+    """The striped partition (token t on device t mod n) at the 128K/8 GQA
+    shape: every block is near the diagonal, so every tile of every step is
+    partially masked."""
+    import torch
+    wl = W["striped128k_8dev_gqa"]
+    rows = sample_rows(wl, 40, seed=100 + rank)
+    share, ref_o, ref_l = _oracle_for(wl, rank, rows)
+    out, lse = harness.run_forward(share, copy_stream=_copy_stream())
+    torch.cuda.synchronize()
+    _check(out, lse, rows, ref_o, ref_l, wl.dtype)
+    assert torch.isfinite(lse).all() and torch.isfinite(out.float()).all()
