@@ -32,6 +32,8 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3         # MI355X fp32 vector
+REALTIME_GHZ = 0.1              # s_memrealtime counts a constant 100 MHz reference clock
+SMALL_SHARE_PAIRS = 1 << 27     # rows x heads x keys up to which the oracle times the whole share
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 DEFAULT_WORKLOAD = "zigzag128k_8dev_gqa"
 
@@ -87,6 +89,82 @@ def cpu_baseline(wl, rank, budget_s=12.0):
                   f"float64 full softmax over all {wl.total_len} global keys, {spent:.1f} s of CPU time; "
                   f"effective FLOPs counted as for the GPU",
     }
+
+
+def cpu_baseline_full(wl, rank):
+    """Time the float64 CPU oracle on the whole share (every local row of every
+    query head), with all BLAS threads and with one; for shares small enough
+    to finish in seconds."""
+    import oracle
+    import ring_inputs
+    from threadpoolctl import threadpool_info, threadpool_limits
+    positions = oracle.device_positions(wl.partition, wl.world, rank, wl.local_len)
+    k_pos = np.arange(wl.total_len)
+    G = wl.heads_q // wl.heads_kv
+    vis = oracle.visible_pair_count(positions, k_pos, wl.causal)
+    flops = 4.0 * wl.head_dim * vis * wl.heads_q * wl.batch
+
+    def run():
+        t0 = time.perf_counter()
+        for b in range(wl.batch):
+            for g in range(wl.heads_kv):
+                kh = ring_inputs.head(wl, "k", b, g)
+                vh = ring_inputs.head(wl, "v", b, g)
+                for h in range(g * G, (g + 1) * G):
+                    q = ring_inputs.rows(wl, "q", b, h, positions)
+                    oracle.attention_rows(q, positions, kh, vh, k_pos, wl.causal)
+        return time.perf_counter() - t0
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    t_all = run()
+    with threadpool_limits(limits=1, user_api="blas"):
+        t_one = run()
+    what = (f"the full share: {wl.local_len} rows of device {rank} x {wl.heads_q} query heads x batch {wl.batch}, "
+            f"float64 full softmax over all {wl.total_len} global keys (input generation included)")
+    return {
+        "value": flops / t_all / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"{what}, {t_all:.2f} s",
+        "single_thread": {"value": flops / t_one / 1e12, "unit": "TFLOP/s", "cores": 1, "seconds": round(t_one, 3)},
+    }
+
+
+def load_balance(wl):
+    """Visible (query, key) pairs of every device over the whole ring, per
+    (batch, head): the work each device does for its rows."""
+    from ring_attention_blockwise_amd import harness
+    per_dev = [sum(harness.step_pairs(wl, r)) for r in range(wl.world)]
+    mean = sum(per_dev) / len(per_dev)
+    return {"partition": wl.partition, "max_over_mean": round(max(per_dev) / mean, 4),
+            "min_over_mean": round(min(per_dev) / mean, 4),
+            "pairs_max": int(max(per_dev)), "pairs_min": int(min(per_dev))}
+
+
+def mfma_probe(blocks=256 * 8, iters=2048, reps=3):
+    """Dense bf16 MFMA rate and shader clock from the library's matrix-core
+    probe (the step kernel's instruction on register operands, every CU)."""
+    import torch
+    import ring_attention_blockwise_amd as ra
+    dev = torch.device("cuda:0")
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    stamps = torch.zeros(blocks * 4, dtype=torch.int64, device=dev)
+    ra.mfma_probe(blocks, iters, sink, stamps)  # warm-up
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        ra.mfma_probe(blocks, iters, sink, stamps)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    st = stamps.view(blocks, 4).cpu().numpy().astype(np.float64)
+    ratio = (st[:, 1] - st[:, 0]) / np.maximum(st[:, 3] - st[:, 2], 1.0)
+    flops = blocks * 4 * iters * 4 * 32768.0
+    tflops = flops / (best * 1e-3) / 1e12
+    return {"instruction": "v_mfma_f32_32x32x16_bf16", "tflops": round(tflops, 1), "ms": round(best, 4),
+            "frac_of_spec": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "shader_clock_ghz": round(float(np.median(ratio)) * REALTIME_GHZ, 3)}
 
 
 # Sources the bf16 step kernel is built from; a counter summary is only used
@@ -405,10 +483,18 @@ def main():
     hbm = hbm_kernels(share)
     log(f"HBM-bound pieces: {hbm}")
 
+    probe = mfma_probe()
+    log(f"matrix-core probe: {probe}")
+    balance = load_balance(wl)
+
     cpu = None
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(wl, rank)
+        if wl.local_len * wl.heads_q * wl.batch * wl.total_len <= SMALL_SHARE_PAIRS:
+            log("timing the CPU oracle on the whole share (all threads, then one)")
+            cpu = cpu_baseline_full(wl, rank)
+        else:
+            log("timing the CPU oracle on a bounded sample")
+            cpu = cpu_baseline(wl, rank)
 
     rec = {
         "metric": "effective causal attention TFLOP/s per ring step at 1 GPU; % of bf16 MFMA peak",
@@ -448,6 +534,8 @@ def main():
         "graph_forward": {"ms_per_forward": round(graph_ms, 4),
                           "value": round(total_flops / (graph_ms * 1e-3) / 1e12, 3)},
         "hbm_kernels": hbm,
+        "mfma_probe": dict(probe, step_kernel_frac_of_probe=round(achieved / probe["tflops"], 4) if bf16 else None),
+        "load_balance": balance,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

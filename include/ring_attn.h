@@ -318,6 +318,21 @@ int ring_attn_event_elapsed_ms(void* start, void* stop, float* ms);
 int ring_attn_events_destroy(int32_t n, void* const* events);
 int ring_attn_synchronize(void* stream);
 
+/* Measurement aid (not part of the attention path): the dense bf16 matrix-core
+ * rate and shader clock of this device, with the instruction the step kernels
+ * use. Enqueues `blocks` workgroups of 4 waves on `stream`; every wave issues
+ * iters x 4 independent v_mfma_f32_32x32x16_bf16 (32 x 32 x 16 products,
+ * 32768 FLOP each) on register operands, so the launch performs
+ * blocks * 4 * iters * 4 * 32768 FLOP. Caller-owned device buffers:
+ *   sink   [blocks * 256] float — the accumulators (keeps every product live);
+ *   stamps [blocks * 4] uint64 — per workgroup, wave 0's shader clock counter
+ *          (s_memtime) at the start and end of its loop, then the constant
+ *          reference counter (s_memrealtime) at the same two points; the ratio
+ *          of the differences times the reference rate is the shader clock.
+ * Returns RA_ERR_INVALID_ARG for blocks <= 0, iters <= 0 or a NULL buffer,
+ * RA_ERR_HIP if the launch fails; nothing is enqueued on error. */
+int ring_attn_mfma_probe(int32_t blocks, int32_t iters, float* sink, uint64_t* stamps, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -32,7 +32,7 @@ EXPORTED = (
     "ring_attn_events_create", "ring_attn_event_elapsed_ms", "ring_attn_events_destroy",
     "ring_attn_synchronize", "ring_attn_ulysses_workspace_size", "ring_attn_ulysses_forward",
     "ring_attn_backward_prep", "ring_attn_backward_step", "ring_attn_backward_workspace_size",
-    "ring_attn_backward",
+    "ring_attn_backward", "ring_attn_mfma_probe",
 )
 
 
@@ -103,6 +103,7 @@ def lib() -> ctypes.CDLL:
             "ring_attn_event_elapsed_ms": (ctypes.c_int, [P, P, ctypes.POINTER(ctypes.c_float)]),
             "ring_attn_events_destroy": (ctypes.c_int, [I32, P]),
             "ring_attn_synchronize": (ctypes.c_int, [P]),
+            "ring_attn_mfma_probe": (ctypes.c_int, [I32, I32, P, P, P]),
             "ring_attn_ulysses_workspace_size": (SZ, [UD]),
             "ring_attn_ulysses_forward": (ctypes.c_int, [UD, P, P, P, P, P, P, SZ, P]),
             "ring_attn_backward_prep": (ctypes.c_int, [SD, P, P, P, P, P]),
@@ -418,3 +419,12 @@ class StepEvents:
 
 def synchronize(stream=None):
     _check(lib().ring_attn_synchronize(_stream(stream)), "synchronize")
+
+
+def mfma_probe(blocks: int, iters: int, sink, stamps, stream=None):
+    """Enqueue the matrix-core probe (ring_attn_mfma_probe): ``sink`` float32 [blocks*256] and
+    ``stamps`` int64 [blocks*4] on the GPU; it performs blocks*4*iters*4*32768 FLOP."""
+    torch = _torch()
+    _check(lib().ring_attn_mfma_probe(int(blocks), int(iters), _ptr(sink, torch.float32, (blocks * 256,), "sink"),
+                                      _ptr(stamps, torch.int64, (blocks * 4,), "stamps"), _stream(stream)),
+           "mfma_probe")

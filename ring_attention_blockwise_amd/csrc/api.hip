@@ -214,11 +214,16 @@ int32_t owner_of(const ra_ring_desc* d, int32_t step) {
 
 }  // namespace
 
+// Launcher of the matrix-core probe (probe.hip).
+namespace ra {
+hipError_t launch_mfma_probe(int32_t blocks, int32_t iters, float* sink, uint64_t* stamps, hipStream_t s);
+}  // namespace ra
+
 extern "C" {
 
 const char* ring_attn_last_error(void) { return g_last_error; }
 
-int32_t ring_attn_abi_version(void) { return 102; }
+int32_t ring_attn_abi_version(void) { return 103; }
 
 int ring_attn_partition_segments(int32_t partition, int32_t world, int32_t rank, int64_t local_len,
                                  ra_segment* segs, int32_t* n_segs) {
@@ -917,6 +922,13 @@ int ring_attn_event_elapsed_ms(void* start, void* stop, float* ms) {
   if (!start || !stop || !ms) return fail(RA_ERR_INVALID_ARG, "NULL argument");
   hipError_t e = hipEventElapsedTime(ms, static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop));
   return e == hipSuccess ? RA_OK : hip_fail(e, "hipEventElapsedTime");
+}
+
+int ring_attn_mfma_probe(int32_t blocks, int32_t iters, float* sink, uint64_t* stamps, void* stream) {
+  if (blocks <= 0 || iters <= 0) return fail(RA_ERR_INVALID_ARG, "blocks and iters must be positive");
+  if (!sink || !stamps) return fail(RA_ERR_INVALID_ARG, "NULL buffer");
+  const hipError_t e = ra::launch_mfma_probe(blocks, iters, sink, stamps, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RA_OK : hip_fail(e, "mfma probe launch");
 }
 
 int ring_attn_events_destroy(int32_t n, void* const* events) {

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert ra.lib().ring_attn_abi_version() == 102
+    assert ra.lib().ring_attn_abi_version() == 103
 
 
 def _expand(segs):
@@ -234,3 +234,12 @@ def test_partition_rejects_bad_input():
         ra.partition_segments("contiguous", 4, 4, 16)
     with pytest.raises(KeyError):
         ra.partition_segments("diagonal", 4, 0, 16)
+
+
+def test_mfma_probe_rejects_bad_arguments():
+    L = ra.lib()
+    fake = ctypes.c_void_p(16)  # never dereferenced: validation comes first
+    assert L.ring_attn_mfma_probe(0, 1, fake, fake, None) == ra.ERR_INVALID_ARG
+    assert L.ring_attn_mfma_probe(1, 0, fake, fake, None) == ra.ERR_INVALID_ARG
+    assert L.ring_attn_mfma_probe(1, 1, None, fake, None) == ra.ERR_INVALID_ARG
+    assert L.ring_attn_mfma_probe(1, 1, fake, None, None) == ra.ERR_INVALID_ARG
