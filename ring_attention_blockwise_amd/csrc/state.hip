@@ -6,11 +6,24 @@
 // O' = O e^(M-M') + ...) applied to two partial states; finalize is that
 // page's closing O / L plus the log-sum-exp. All three are HBM-bound
 // streaming passes: one workgroup of 256 threads handles 16 rows, 16 threads
-// per row, each thread moving 16-byte vectors along head_dim.
+// per row, each thread moving 16-byte vectors along head_dim. Every element
+// of O is touched once, so its loads and stores carry the non-temporal hint
+// (measured: merge 5.5 -> 6.5 TB/s, finalize 5.9 -> 6.5 TB/s at the 128K/8
+// share's shapes, the level of the D2D copy).
 #include "common.h"
 
 namespace ra {
 namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 stream_load(const float4* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
+__device__ __forceinline__ void stream_store(float4* p, f32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+}
 
 constexpr int kThreads = 256;
 constexpr int kThreadsPerRow = 16;
@@ -40,12 +53,8 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(float* __restrict__ o_a
   const float4* ob = reinterpret_cast<const float4*>(o_b + row * D);
 #pragma unroll
   for (int i = sub; i < D / 4; i += kThreadsPerRow) {
-    float4 x = oa[i], y = ob[i];
-    x.x = wa * x.x + wb * y.x;
-    x.y = wa * x.y + wb * y.y;
-    x.z = wa * x.z + wb * y.z;
-    x.w = wa * x.w + wb * y.w;
-    oa[i] = x;
+    const f32x4 x = stream_load(oa + i), y = stream_load(ob + i);
+    stream_store(oa + i, wa * x + wb * y);
   }
   if (sub == 0) {
     l_a[row] = wa * l_a[row] + wb * l_b[row];
@@ -65,18 +74,13 @@ __global__ void __launch_bounds__(kThreads) finalize_kernel(const float* __restr
   const float4* src = reinterpret_cast<const float4*>(o + row * D);
 #pragma unroll
   for (int i = sub; i < D / 4; i += kThreadsPerRow) {
-    float4 x = src[i];
-    x.x *= inv;
-    x.y *= inv;
-    x.z *= inv;
-    x.w *= inv;
+    const f32x4 x = stream_load(src + i) * inv;
     if constexpr (BF16) {
-      uint2 packed;
-      packed.x = (uint32_t)f32_to_bf16_bits(x.x) | ((uint32_t)f32_to_bf16_bits(x.y) << 16);
-      packed.y = (uint32_t)f32_to_bf16_bits(x.z) | ((uint32_t)f32_to_bf16_bits(x.w) << 16);
-      reinterpret_cast<uint2*>(static_cast<unsigned short*>(out) + row * D)[i] = packed;
+      const u32x2 packed = {(uint32_t)f32_to_bf16_bits(x.x) | ((uint32_t)f32_to_bf16_bits(x.y) << 16),
+                            (uint32_t)f32_to_bf16_bits(x.z) | ((uint32_t)f32_to_bf16_bits(x.w) << 16)};
+      __builtin_nontemporal_store(packed, reinterpret_cast<u32x2*>(static_cast<unsigned short*>(out) + row * D) + i);
     } else {
-      reinterpret_cast<float4*>(static_cast<float*>(out) + row * D)[i] = x;
+      stream_store(reinterpret_cast<float4*>(static_cast<float*>(out) + row * D) + i, x);
     }
   }
   if (sub == 0 && lse != nullptr) lse[row] = finalize_lse(m[row], lr);
@@ -90,7 +94,7 @@ __global__ void __launch_bounds__(kThreads) init_state_kernel(float* __restrict_
   if (row >= rows) return;
   float4* dst = reinterpret_cast<float4*>(o + row * D);
 #pragma unroll
-  for (int i = sub; i < D / 4; i += kThreadsPerRow) dst[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = sub; i < D / 4; i += kThreadsPerRow) stream_store(dst + i, f32x4{0.f, 0.f, 0.f, 0.f});
   if (sub == 0) {
     m[row] = -INFINITY;
     l[row] = 0.0f;
