@@ -211,13 +211,14 @@ size_t ring_attn_ulysses_workspace_size(const ra_ulysses_desc* desc);
  *   q_shards[j], out_shards[j]   [B, Hq,  L/world, d] dtype: device j's rows
  *                                j*L/world .. (j+1)*L/world - 1.
  *   k_shards[j], v_shards[j]     [B, Hkv, L/world, d] dtype.
- *   lse_shards[j]                [B, Hq,  L/world] fp32; the array may be NULL.
+ *   lse_shards[j]                [B, Hq,  L/world] fp32, 4-byte aligned; the array may be NULL.
  *   (HOST arrays of `world` DEVICE pointers.)
  * Reads query heads rank*Hq/world .. (rank+1)*Hq/world - 1 (and the matching
  * KV heads) of every shard and writes the same heads of every out (and lse)
  * shard; running every rank fills the outputs. All work is enqueued on
- * `stream`: gather (first all-to-all), one attention launch (init and
- * finalize fused), scatter (second all-to-all). */
+ * `stream`: gather (first all-to-all: one copy kernel per tensor), one
+ * attention launch (init and finalize fused), scatter (second all-to-all).
+ * Q/K/V/out shards must be 16-byte aligned (RA_ERR_INVALID_ARG otherwise). */
 int ring_attn_ulysses_forward(const ra_ulysses_desc* desc, const void* const* q_shards,
                               const void* const* k_shards, const void* const* v_shards,
                               void* const* out_shards, float* const* lse_shards,

@@ -13,6 +13,7 @@
 #include "backward.h"
 #include "common.h"
 #include "ring_attn.h"
+#include "ulysses_leg.h"
 
 namespace {
 
@@ -567,27 +568,31 @@ void ulysses_layout(const ra_ulysses_desc* d, UlyssesLayout* L) {
   L->total = off + 256;  // room to align the caller's base pointer
 }
 
-// One all-to-all leg for this device, as strided copies: for every shard j
-// and batch b, `rows` consecutive heads of `width` bytes each move between
-// the shard (head pitch `shard_pitch`, first head `shard_head`, heads per
-// batch `shard_heads`) and the head-sharded buffer (head pitch `full_pitch`,
-// segment j at byte j * width). to_shards picks the direction.
+// One all-to-all leg for this device: for every shard j and batch b, `rows`
+// consecutive heads of `width` bytes each move between the shard (head pitch
+// `width`, first head `shard_head`, heads per batch `shard_heads`) and the
+// head-sharded buffer (head pitch `full_pitch`, segment j at byte j * width).
+// shards_out picks the direction. One copy kernel per 64 shards.
 hipError_t all_to_all_leg(const ra_ulysses_desc* d, char* full, const char* const* shards_in,
                           char* const* shards_out, int64_t rows, int64_t shard_heads, int64_t shard_head,
                           size_t width, size_t full_pitch, hipStream_t s) {
-  for (int j = 0; j < d->world; ++j)
-    for (int b = 0; b < d->batch; ++b) {
-      char* fptr = full + ((size_t)b * rows) * full_pitch + (size_t)j * width;
-      const size_t shard_off = ((size_t)b * shard_heads + shard_head) * width;
-      hipError_t e;
-      if (shards_out)
-        e = hipMemcpy2DAsync(shards_out[j] + shard_off, width, fptr, full_pitch, width, rows,
-                             hipMemcpyDeviceToDevice, s);
-      else
-        e = hipMemcpy2DAsync(fptr, full_pitch, shards_in[j] + shard_off, width, width, rows,
-                             hipMemcpyDeviceToDevice, s);
-      if (e != hipSuccess) return e;
-    }
+  for (int j0 = 0; j0 < d->world; j0 += ra::kA2AShards) {
+    ra::A2ALeg a{};
+    a.full = full;
+    a.j0 = j0;
+    a.nshards = d->world - j0 < ra::kA2AShards ? d->world - j0 : ra::kA2AShards;
+    a.to_shards = shards_out != nullptr;
+    for (int k = 0; k < a.nshards; ++k)
+      a.shard[k] = shards_out ? shards_out[j0 + k] : const_cast<char*>(shards_in[j0 + k]);
+    a.batch = d->batch;
+    a.rows = rows;
+    a.shard_heads = shard_heads;
+    a.shard_head = shard_head;
+    a.width = (int64_t)width;
+    a.full_pitch = (int64_t)full_pitch;
+    const hipError_t e = ra::launch_a2a_leg(a, s);
+    if (e != hipSuccess) return e;
+  }
   return hipSuccess;
 }
 
@@ -615,6 +620,8 @@ int ring_attn_ulysses_forward(const ra_ulysses_desc* d, const void* const* q_sha
       if (!aligned16(q_shards[j]) || !aligned16(k_shards[j]) || !aligned16(v_shards[j]) || !aligned16(out_shards[j]))
         return fail(RA_ERR_INVALID_ARG, "shard %d is not 16-byte aligned", j);
       if (lse_shards && !lse_shards[j]) return fail(RA_ERR_INVALID_ARG, "lse shard %d pointer is NULL", j);
+      if (lse_shards && (reinterpret_cast<uintptr_t>(lse_shards[j]) & 3u) != 0)
+        return fail(RA_ERR_INVALID_ARG, "lse shard %d is not 4-byte aligned", j);
     }
   UlyssesLayout L;
   ulysses_layout(d, &L);

@@ -125,6 +125,11 @@ ULYSSES_WORKLOADS = {
         name="ulysses512_2dev_f32", batch=2, heads_q=4, heads_kv=2, head_dim=64, dtype="f32",
         causal=False, partition="contiguous", world=2, local_len=256, seed=1007, ranks=(0, 1),
         description="Ulysses, non-causal, 512 tokens over 2 devices, B2, 4 Q / 2 KV heads, d64 fp32"),
+    "ulysses990_3dev_ragged": Workload(
+        name="ulysses990_3dev_ragged", batch=2, heads_q=6, heads_kv=3, head_dim=64, dtype="bf16",
+        causal=True, partition="contiguous", world=3, local_len=330, seed=1031, ranks=(0, 1, 2),
+        description="Ulysses, causal, 990 tokens over 3 devices (330 per shard: ragged tiles, LSE shards "
+                    "not a multiple of 16 bytes), B2, 6 Q / 3 KV heads, d64 bf16"),
     "ulysses128k_8dev_gqa": Workload(
         name="ulysses128k_8dev_gqa", batch=1, heads_q=32, heads_kv=8, head_dim=128, dtype="bf16",
         causal=True, partition="contiguous", world=8, local_len=16384, seed=1003, ranks=(0,),

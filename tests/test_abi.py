@@ -193,6 +193,9 @@ def test_ulysses_workspace_and_validation():
     assert rc == ra.ERR_INVALID_ARG
     rc = L.ring_attn_ulysses_forward(ctypes.byref(ud), None, shards, shards, shards, None, FAKE, ws, None)
     assert rc == ra.ERR_INVALID_ARG
+    odd_lse = (ctypes.c_void_p * 4)(*([0x10000] * 3 + [0x10002]))  # fp32 LSE shards must be 4-byte aligned
+    rc = L.ring_attn_ulysses_forward(ctypes.byref(ud), shards, shards, shards, shards, odd_lse, FAKE, ws, None)
+    assert rc == ra.ERR_INVALID_ARG
 
 
 def test_backward_workspace_and_validation():

@@ -54,7 +54,7 @@ def _oracle_rows(wl, b, h, positions):
     return oracle.attention_rows(q, positions, k, v, np.arange(wl.total_len), wl.causal)
 
 
-@pytest.mark.parametrize("name", ["ulysses2k_4dev_gqa", "ulysses512_2dev_f32"])
+@pytest.mark.parametrize("name", ["ulysses2k_4dev_gqa", "ulysses512_2dev_f32", "ulysses990_3dev_ragged"])
 def test_small_ulysses_every_row(gpu, name):
     import torch
     wl = U[name]
