@@ -136,7 +136,7 @@ __device__ __forceinline__ void sched_mfma_reads_valu() {
 // ============================================================================
 constexpr int kQWaves = 8;
 constexpr int kQRows = kQWaves * 32;
-constexpr int kQStages = 3;
+constexpr int kQStages = 4;  // a tile is read row-wise in M_t and transposed in M_{t+1}
 template <int D>
 __global__ void __launch_bounds__(kQWaves * 64) bwd_dq_kernel(BwdArgs a, int32_t q_tiles) {
   using L = BL<D>;
@@ -245,21 +245,66 @@ __global__ void __launch_bounds__(kQWaves * 64) bwd_dq_kernel(BwdArgs a, int32_t
   for (int db = 0; db < kDB; ++db)
 #pragma unroll
     for (int j = 0; j < 16; ++j) dqa[db][j] = 0.0f;
+  f32x16 sacc[2], pacc[2];
+  bf16x8 dsf[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      sacc[kb][j] = 0.0f;
+      pacc[kb][j] = 0.0f;
+    }
+    dsf[kb][0] = bf16x8{};
+    dsf[kb][1] = bf16x8{};
+  }
 
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  for (int t = 0; t < ntiles; ++t) {
-    // Tile t's copies have landed once at most the next tile's are in flight;
-    // the barrier publishes it and ends every read of tile t-1, whose stage
-    // the copies of tile t+2 then reuse.
-    if (t + 1 < ntiles)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kQCopies) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    asm volatile("s_barrier" ::: "memory");
-    if (t + 2 < ntiles) issue(t + 2);
-    const uint32_t so = (uint32_t)(t % kQStages) * kQStageB;
+  // Per wave the work is M_0 V_0 M_1 V_1 ... V_{n-1} M_n with M_v = (dQ of
+  // tile v-1, S and dP of tile v) on the matrix cores and V_v the vector work
+  // of tile v (mask, P, dS). Waves 0-3 (group 0) run item i in phase i, waves
+  // 4-7 (group 1) in phase i+1, so while one wave of a SIMD issues MFMAs its
+  // partner works on the vector ALUs. Only even phases start with a barrier
+  // (every wave passes n+1 of them). Tile t sits in stage t % 4: it is read
+  // row-wise in M_t and transposed in M_{t+1}, by group 1 as late as phase
+  // 2t+3, and refilled with tile t+4 after the barrier of phase 2t+4: group 0
+  // copies its half of tile v+2 after V_v (phase 2v+1), group 1 its half of
+  // tile v+3 after V_v (phase 2v+2). At even phase 2u each wave waits for its
+  // copies of tile u (those of tile u+1 may stay in flight) and the barrier
+  // publishes it.
+  const int group = wave >> 2;
+  int ph = 0;
+  auto next_phase = [&]() {
+    const int u = ph >> 1;
+    if ((ph & 1) == 0) {
+      if (u < ntiles) {
+        if (u + 1 < ntiles)
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kQCopies) : "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      asm volatile("s_barrier" ::: "memory");
+    }
+    ++ph;
+  };
 
-    f32x16 sacc[2], pacc[2];
+  auto iteration = [&](int v) {
+    const uint32_t so = (uint32_t)(v % kQStages) * kQStageB;
+    const uint32_t sp = (uint32_t)((v + kQStages - 1) % kQStages) * kQStageB;
+    next_phase();
+    // ---- M_v: dQ^T += K^T dS^T (tile v-1), then S^T = K Q^T and dP^T = V dO^T
+    // (tile v): dS of tile v-1 is dead before the accumulators of tile v are
+    // live, which keeps the wave within its registers. On the last iteration
+    // (v == ntiles) the S and dP products read a stage holding an older tile
+    // and are never used.
+    if (v > 0) {
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+          const bf16x8 kt = read_tr(lo, hi, db, sp + kc * 16 * kRowB);
+          dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsf[kc >> 1][kc & 1], dqa[db], 0, 0, 0);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -276,38 +321,45 @@ __global__ void __launch_bounds__(kQWaves * 64) bwd_dq_kernel(BwdArgs a, int32_t
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sacc[kb], 0, 0, 0);
         pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, of[c], pacc[kb], 0, 0, 0);
       }
-
-    const bool first_range = t < plan.r0.ntiles;
-    const int32_t start = tile_start(t);
-    if (start + 64 > (first_range ? plan.r0.full : plan.r1.full)) {
-      const int32_t lim = (first_range ? vend0 : vend1) - start;  // keys [0, lim) are visible
+    if (v < ntiles) {
+      next_phase();
+      // ---- V_v: P and dS of tile v, packed as the B operand of dQ
+      const bool first_range = v < plan.r0.ntiles;
+      const int32_t start = tile_start(v);
+      if (start + 64 > (first_range ? plan.r0.full : plan.r1.full)) {
+        const int32_t lim = (first_range ? vend0 : vend1) - start;  // keys [0, lim) are visible
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int key = kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
+            if (key >= lim) sacc[kb][j] = -INFINITY;
+          }
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const int key = kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
-          if (key >= lim) sacc[kb][j] = -INFINITY;
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][j], sl2, c2));
+          sacc[kb][j] = p * (pacc[kb][j] + e_row);
         }
-    }
-    bf16x8 dsf[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][j], sl2, c2));
-        sacc[kb][j] = p * (pacc[kb][j] + e_row);
+        dsf[kb][0] = pack_p(sacc[kb], 0);
+        dsf[kb][1] = pack_p(sacc[kb], 8);
       }
-      dsf[kb][0] = pack_p(sacc[kb], 0);
-      dsf[kb][1] = pack_p(sacc[kb], 8);
+      const int t = v + (group == 1 ? 3 : 2);
+      if (t >= 2 && t < ntiles) issue(t);
     }
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc)
-#pragma unroll
-      for (int db = 0; db < kDB; ++db) {
-        const bf16x8 kt = read_tr(lo, hi, db, so + kc * 16 * kRowB);
-        dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsf[kc >> 1][kc & 1], dqa[db], 0, 0, 0);
-      }
+  };
+
+  // Q, dO, the row terms and the first tiles are in registers / LDS before
+  // the loop.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  if (group == 1) {  // group 1 starts one phase late
+    next_phase();
+    if (2 < ntiles) issue(2);
   }
+  for (int v = 0; v <= ntiles; ++v) iteration(v);
+  if (group == 0) next_phase();  // group 0 ends one phase early
 
   if (!valid) return;
   float* dst = a.dq + srow * kD;
