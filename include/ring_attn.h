@@ -35,7 +35,7 @@
  *            is written. A failed HIP call returns RA_ERR_HIP.
  *            ring_attn_last_error() gives a message for the calling thread.
  * Sizes.     Row counts (q_len, kv_len, local_len, seq_len) are at most 2^30,
- *            and batch x heads x rows at most 2^35 on the query and on the
+ *            and batch x heads x rows at most 2^34 on the query and on the
  *            key/value side, else RA_ERR_INVALID_ARG (every launch's grid then
  *            fits in 32 bits).
  * GQA.       Query head h reads KV head h / (heads_q / heads_kv) — contiguous

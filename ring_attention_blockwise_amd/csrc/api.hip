@@ -32,7 +32,7 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 constexpr int64_t kMaxRows = (int64_t)1 << 30;
-constexpr int64_t kMaxStateRows = (int64_t)1 << 35;  // batch x heads x rows
+constexpr int64_t kMaxStateRows = (int64_t)1 << 34;  // batch x heads x rows
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -55,7 +55,7 @@ int check_shape(const ra_step_desc* d, bool need_kv) {
   // every launch's work-item count and grid size stay within 32 bits
   if ((int64_t)d->batch * d->heads_q > kMaxStateRows / (d->q_len > 0 ? d->q_len : 1) ||
       (need_kv && (int64_t)d->batch * d->heads_kv > kMaxStateRows / (d->kv_len > 0 ? d->kv_len : 1)))
-    return fail(RA_ERR_INVALID_ARG, "batch x heads x rows exceeds 2^35");
+    return fail(RA_ERR_INVALID_ARG, "batch x heads x rows exceeds 2^34");
   if (d->dtype != RA_F32 && d->dtype != RA_BF16) return fail(RA_ERR_UNSUPPORTED, "dtype %d not supported", d->dtype);
   if (d->head_dim != 64 && d->head_dim != 128)
     return fail(RA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);

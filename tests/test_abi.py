@@ -249,14 +249,14 @@ def test_mfma_probe_rejects_bad_arguments():
 
 
 def test_total_rows_beyond_the_grid_limit_are_rejected():
-    """batch x heads x rows above 2^35 would overflow 32-bit launch grids:
+    """batch x heads x rows above 2^34 would overflow 32-bit launch grids:
     rejected on the host (no GPU work, fake pointers never touched)."""
     L = ra.lib()
-    big = ra.step_desc(1 << 14, 1 << 10, 1 << 10, 128, 1 << 12, 1 << 12, causal=False)  # 2^36 rows
+    big = ra.step_desc(1 << 13, 1 << 10, 1 << 10, 128, 1 << 12, 1 << 12, causal=False)  # 2^35 rows
     assert L.ring_attn_visible_pairs(ctypes.byref(big)) == -1
     args = [FAKE] * 6
     assert L.ring_attn_step(ctypes.byref(big), *args, 1, None) == ra.ERR_INVALID_ARG
-    ok = ra.step_desc(1 << 13, 1 << 10, 1 << 10, 128, 1 << 12, 1 << 12, causal=False)  # 2^35 rows: allowed
+    ok = ra.step_desc(1 << 12, 1 << 10, 1 << 10, 128, 1 << 12, 1 << 12, causal=False)  # 2^34 rows: allowed
     assert L.ring_attn_visible_pairs(ctypes.byref(ok)) == (1 << 12) * (1 << 12)
-    rd = ra.ring_desc(1 << 14, 1 << 10, 1 << 10, 128, 1 << 12, 8, 0, partition="contiguous")
+    rd = ra.ring_desc(1 << 13, 1 << 10, 1 << 10, 128, 1 << 12, 8, 0, partition="contiguous")
     assert L.ring_attn_forward_workspace_size(ctypes.byref(rd)) == 0
