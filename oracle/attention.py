@@ -39,7 +39,10 @@ def attention_rows(q, q_pos, k, v, k_pos, causal: bool, scale: float | None = No
     """float64 softmax attention of query rows ``q`` [R, d] over keys ``k`` [L, d].
 
     Returns (O [R, dv], LSE [R]). Rows are evaluated independently, ``row_group``
-    at a time, each over all of its visible keys at once.
+    at a time (in order of position), each over all of its visible keys at
+    once. When the mask is causal and ``k_pos`` is ascending, keys past the
+    last position a group's rows can see carry weight exactly zero for every
+    row of the group and are left out of its products.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -51,21 +54,27 @@ def attention_rows(q, q_pos, k, v, k_pos, causal: bool, scale: float | None = No
     R = q.shape[0]
     out = np.zeros((R, v.shape[1]), dtype=np.float64)
     lse = np.full(R, -np.inf, dtype=np.float64)
+    ascending = bool(causal) and bool(np.all(k_pos[1:] >= k_pos[:-1]))
+    order = np.argsort(q_pos, kind="stable")
     for r0 in range(0, R, row_group):
-        r1 = min(R, r0 + row_group)
-        s = (q[r0:r1] @ k.T) * scale
+        idx = order[r0:min(R, r0 + row_group)]
+        n = len(k_pos)
+        if ascending and len(idx):
+            n = int(np.searchsorted(k_pos, q_pos[idx].max(), side="right"))
+        kk, vv, kp = k[:n], v[:n], k_pos[:n]
+        s = (q[idx] @ kk.T) * scale
         if causal:
-            visible = k_pos[None, :] <= q_pos[r0:r1, None]
+            visible = kp[None, :] <= q_pos[idx, None]
             s = np.where(visible, s, -np.inf)
-        m = s.max(axis=1)
+        m = s.max(axis=1) if n else np.full(len(idx), -np.inf)
         has = np.isfinite(m)
         p = np.exp(s - np.where(has, m, 0.0)[:, None])
         l = p.sum(axis=1)
-        o = (p @ v) / np.where(has, l, 1.0)[:, None]
+        o = (p @ vv) / np.where(has, l, 1.0)[:, None]
         o[~has] = 0.0
-        out[r0:r1] = o
+        out[idx] = o
         with np.errstate(divide="ignore"):
-            lse[r0:r1] = np.where(has, m + np.log(np.where(has, l, 1.0)), -np.inf)
+            lse[idx] = np.where(has, m + np.log(np.where(has, l, 1.0)), -np.inf)
     return out, lse
 
 

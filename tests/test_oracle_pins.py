@@ -123,6 +123,15 @@ def test_matches_torch_sdpa_with_gqa(causal, heads):
         o, lse = oracle.attention_rows(q[h], q_pos, k[g], v[g], k_pos, causal)
         np.testing.assert_allclose(o, ref_o[h], atol=1e-12, rtol=1e-12)
         np.testing.assert_allclose(lse, ref_lse[h], atol=1e-12, rtol=1e-12)
+        # rows in shuffled order over several row groups (the causal key
+        # prefix of each group is cut at its last visible position), and the
+        # keys handed over in shuffled order (no prefix cut): same rows
+        perm = rng.permutation(R)
+        kperm = rng.permutation(L)
+        for kk, vv, kp in ((k[g], v[g], k_pos), (k[g][kperm], v[g][kperm], k_pos[kperm])):
+            o2, lse2 = oracle.attention_rows(q[h][perm], q_pos[perm], kk, vv, kp, causal, row_group=7)
+            np.testing.assert_allclose(o2, ref_o[h][perm], atol=1e-12, rtol=1e-12)
+            np.testing.assert_allclose(lse2, ref_lse[h][perm], atol=1e-12, rtol=1e-12)
 
 
 def test_lse_matches_scipy_logsumexp_at_large_logits():
@@ -241,6 +250,17 @@ def test_zigzag_positions_match_stated_chunks():
         cl = g["chunk_len"]
         expect = np.concatenate([np.arange(a * cl, (a + 1) * cl), np.arange(b * cl, (b + 1) * cl)])
         np.testing.assert_array_equal(pos, expect)
+
+
+def test_striped_positions_match_stated_tokens():
+    """GPU 0 of a 4-GPU striped split holds tokens 0, 4, 8, ... (the page's
+    example); together with every position being covered once, this fixes
+    the stride and rules out a contiguous or zigzag map under that name."""
+    g = _load("striped_4gpu_positions.json")
+    for local_len in (3, 8, 64):
+        pos = oracle.device_positions("striped", g["world"], g["rank"], local_len)
+        np.testing.assert_array_equal(pos[:3], g["first_positions"])
+        np.testing.assert_array_equal(np.diff(pos), np.full(local_len - 1, g["world"]))
 
 
 @pytest.mark.parametrize("partition", ["contiguous", "zigzag", "striped"])
