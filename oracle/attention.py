@@ -62,13 +62,18 @@ def attention_rows(q, q_pos, k, v, k_pos, causal: bool, scale: float | None = No
         if ascending and len(idx):
             n = int(np.searchsorted(k_pos, q_pos[idx].max(), side="right"))
         kk, vv, kp = k[:n], v[:n], k_pos[:n]
-        s = (q[idx] @ kk.T) * scale
+        s = q[idx] @ kk.T
+        s *= scale
         if causal:
-            visible = kp[None, :] <= q_pos[idx, None]
-            s = np.where(visible, s, -np.inf)
+            if ascending:  # each row's visible keys are a prefix of kk
+                for i, e in enumerate(np.searchsorted(kp, q_pos[idx], side="right")):
+                    s[i, e:] = -np.inf
+            else:
+                s[kp[None, :] > q_pos[idx, None]] = -np.inf
         m = s.max(axis=1) if n else np.full(len(idx), -np.inf)
         has = np.isfinite(m)
-        p = np.exp(s - np.where(has, m, 0.0)[:, None])
+        s -= np.where(has, m, 0.0)[:, None]
+        p = np.exp(s, out=s)
         l = p.sum(axis=1)
         o = (p @ vv) / np.where(has, l, 1.0)[:, None]
         o[~has] = 0.0
