@@ -31,10 +31,10 @@ forms, a library routine and invariants (see each function's docstring).
 """
 from .positions import device_positions, partition_table
 from .attention import attention_rows, device_share, visible_pair_count, kv_head_of
-from .backward import attention_backward_rows, device_backward, upstream_rows
+from .backward import attention_backward_rows, device_backward, key_gradients, upstream_rows
 
 __all__ = [
     "device_positions", "partition_table", "attention_rows", "device_share",
     "visible_pair_count", "kv_head_of", "attention_backward_rows", "device_backward",
-    "upstream_rows",
+    "key_gradients", "upstream_rows",
 ]

@@ -67,6 +67,48 @@ def attention_backward_rows(q, q_pos, k, v, k_pos, do, causal: bool, scale: floa
             "p_k": p @ k, "abs_ds_k": np.abs(ds) @ np.abs(k)}
 
 
+def key_gradients(q, q_pos, k, v, k_pos, do, causal: bool, key_index, scale: float | None = None):
+    """The part of dK_j and dV_j that rows ``q`` produce, for the keys
+    ``key_index`` (indices into ``k``) only.
+
+    The row statistics come from all keys: LSE_i and O_i by ``attention_rows``,
+    D_i = dO_i . O_i. Then, at the chosen keys j only: P_ij = exp(s_ij -
+    LSE_i) where visible, dP_ij = dO_i . v_j, dS_ij = P_ij (dP_ij - D_i),
+    dK_j = scale * sum_i dS_ij q_i and dV_j = sum_i P_ij dO_i — the same chain
+    rule as ``attention_backward_rows``, restricted to a few columns, so a few
+    keys of a long sequence cost only the rows that can see them.
+
+    Also returns three sums that size the rounding error of a
+    reduced-precision evaluation (not gradients), per key and column:
+    ``abs_ds_q`` = sum_i |dS_ij| |q_i|, ``p_a_q`` = sum_i P_ij A_i |q_i| with
+    A_i = sum_d |dO_id| |O_id|, and ``p_do`` = sum_i P_ij |dO_i|.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    k_pos = np.asarray(k_pos, dtype=np.int64)
+    key_index = np.asarray(key_index, dtype=np.int64)
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[1])
+    out, lse = attention_rows(q, q_pos, k, v, k_pos, causal, scale)
+    kj, vj, pj = k[key_index], v[key_index], k_pos[key_index]
+    s = (q @ kj.T) * scale
+    visible = np.ones(s.shape, dtype=bool)
+    if causal:
+        visible = pj[None, :] <= q_pos[:, None]
+    has = np.isfinite(lse)
+    p = np.where(visible & has[:, None], np.exp(s - np.where(has, lse, 0.0)[:, None]), 0.0)
+    dp = do @ vj.T
+    delta = np.einsum("rd,rd->r", do, out)
+    ds = p * (dp - delta[:, None])
+    a = (np.abs(do) * np.abs(out)).sum(axis=1)
+    return {"dk": scale * (ds.T @ q), "dv": p.T @ do,
+            "abs_ds_q": np.abs(ds).T @ np.abs(q), "p_a_q": p.T @ (a[:, None] * np.abs(q)),
+            "p_do": p.T @ np.abs(do)}
+
+
 def upstream_rows(wl: "ring_inputs.Workload", b: int, h: int, positions) -> np.ndarray:
     """The seeded upstream gradient dO at the given global positions (float32)."""
     return ring_inputs.rows(wl, "do", b, h, positions)

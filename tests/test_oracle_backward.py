@@ -85,6 +85,18 @@ def test_matches_torch_autograd_with_gqa(causal, heads):
         dv[gh] += r["dv"]
     np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-12, rtol=1e-10)
     np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-12, rtol=1e-10)
+    # the gradients of a few chosen keys alone, rows split in two parts
+    pick = np.array([0, 1, 37, L - 2, L - 1, 50])
+    dk_p = np.zeros((hkv, len(pick), d))
+    dv_p = np.zeros((hkv, len(pick), d))
+    for h in range(hq):
+        gh = oracle.kv_head_of(h, hq, hkv)
+        for rows in (slice(0, 20), slice(20, R)):
+            r = oracle.key_gradients(q[h][rows], q_pos[rows], k[gh], v[gh], k_pos, do[h][rows], causal, pick)
+            dk_p[gh] += r["dk"]
+            dv_p[gh] += r["dv"]
+    np.testing.assert_allclose(dk_p, tk.grad.numpy()[:, pick], atol=1e-12, rtol=1e-10)
+    np.testing.assert_allclose(dv_p, tv.grad.numpy()[:, pick], atol=1e-12, rtol=1e-10)
 
 
 def test_invariants_of_softmax_attention():
@@ -119,6 +131,27 @@ def test_error_terms():
     # one row, keys all positive: |sum_j dS_j k_j| < sum_j |dS_j| k_j unless dS has one sign (it never
     # does: the dS of a row sum to zero), so the bound is strict here
     assert (np.abs(r2["dq"]) < scale * r2["abs_ds_k"]).all()
+
+
+def test_key_error_terms():
+    """Over all keys, each row's softmax weights sum to one, so sum_j p_do_j =
+    sum_i |dO_i| and sum_j p_a_q_j = sum_i A_i |q_i|; |dK_j| <= scale *
+    abs_ds_q_j (triangle inequality), with equality for a single row (one
+    term per key) and strict somewhere for many rows."""
+    rng = np.random.default_rng(17)
+    q, k, v, do, q_pos, k_pos = _case(rng, 24, 50, 8, True)
+    q = np.abs(q)
+    allk = np.arange(50)
+    r = oracle.key_gradients(q, q_pos, k, v, k_pos, do, True, allk)
+    out, _ = oracle.attention_rows(q, q_pos, k, v, k_pos, True)
+    np.testing.assert_allclose(r["p_do"].sum(axis=0), np.abs(do).sum(axis=0), atol=1e-12)
+    a = (np.abs(do) * np.abs(out)).sum(axis=1)
+    np.testing.assert_allclose(r["p_a_q"].sum(axis=0), (a[:, None] * q).sum(axis=0), atol=1e-12)
+    scale = 1 / math.sqrt(8)
+    assert (np.abs(r["dk"]) <= scale * r["abs_ds_q"] + 1e-15).all()
+    assert (np.abs(r["dk"]) < scale * r["abs_ds_q"] - 1e-6).any()
+    one = oracle.key_gradients(q[:1], [49], k, v, k_pos, do[:1], True, allk)
+    np.testing.assert_allclose(np.abs(one["dk"]), scale * one["abs_ds_q"], rtol=1e-12, atol=0)
 
 
 def test_single_visible_key():
