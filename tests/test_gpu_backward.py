@@ -139,9 +139,48 @@ def test_backward_is_deterministic_and_accumulates(gpu):
         assert torch.equal(2 * dk1[j], dk2[j]) and torch.equal(2 * dv1[j], dv2[j])
 
 
+KEY_WINDOW = 1024      # sampled keys sit in the last KEY_WINDOW global positions
+KEYS_PER_HEAD = 64
+DQ_ROWS = 256
+
+
+def _window_keys(wl, seed):
+    """Global positions of the sampled keys: the last KEY_WINDOW positions
+    hold them, at the in-tile offsets of the 128-key workgroup tiles there
+    and seeded random ones, KEYS_PER_HEAD in all."""
+    L = wl.total_len
+    lo = L - KEY_WINDOW
+    base = {lo, lo + 1, L - 2, L - 1}
+    for t in (0, 3, 7):
+        base |= {lo + 128 * t + o for o in (0, 1, 31, 32, 63, 64, 127)}
+    rng = np.random.default_rng(seed)
+    pool = np.setdiff1d(np.arange(lo, L), np.fromiter(base, dtype=np.int64))
+    base |= set(rng.choice(pool, size=KEYS_PER_HEAD - len(base), replace=False).tolist())
+    return np.array(sorted(base), dtype=np.int64)
+
+
+def _block_of_positions(wl):
+    """global position -> (block, local key index) under the workload's partition."""
+    where = np.zeros((wl.total_len, 2), dtype=np.int64)
+    for j in range(wl.world):
+        p = oracle.device_positions(wl.partition, wl.world, j, wl.local_len)
+        where[p, 0] = j
+        where[p, 1] = np.arange(wl.local_len)
+    return where
+
+
 @pytest.mark.parametrize("name,rank", [("zigzag128k_8dev_gqa", 0), ("stress256k_8dev_d64", 7)])
-def test_full_size_backward_sampled_rows_and_identities(gpu, name, rank):
+def test_full_size_backward_sampled_rows_keys_and_identities(gpu, name, rank):
+    """dQ at sampled rows and dK/dV at sampled keys, element by element,
+    against per-element error budgets; the sum identities over every key.
+
+    A key's gradient needs the statistics of every row that sees it, so the
+    sampled keys come from the last KEY_WINDOW positions of the sequence,
+    which only the device's rows at those positions can see; the oracle
+    computes those rows over all keys."""
     import torch
+    from concurrent.futures import ThreadPoolExecutor
+    import sampling
     wl = ring_inputs.WORKLOADS[name]
     dev = torch.device("cuda:0")
     share = harness.build_share(wl, rank, dev)
@@ -152,28 +191,70 @@ def test_full_size_backward_sampled_rows_and_identities(gpu, name, rank):
     dq = harness.run_backward(share, out, lse, d_out, dk, dv, copy_stream=cs)
     torch.cuda.synchronize()
 
-    # dQ rows: each depends on its own row only
-    c = wl.local_len
-    rng = np.random.default_rng(17)
-    rows = sorted({0, 1, 255, 256, c // 2 - 1, c // 2, c - 1} | set(rng.choice(c, 40, replace=False).tolist()))
-    pos = share.q_positions[rows]
-    k_pos = np.arange(wl.total_len)
-    dq_np = dq[:, :, rows].float().cpu().numpy()
-    scale = 1.0 / np.sqrt(wl.head_dim)
-    err = 0.0
+    c, L = wl.local_len, wl.total_len
     group = wl.heads_q // wl.heads_kv
+    scale = 1.0 / np.sqrt(wl.head_dim)
+    k_pos = np.arange(L)
+    qpos = share.q_positions
+
+    # dQ rows (tile and chunk boundaries included)
+    rows = sampling.sample_rows(wl, seed=17, n_rows=DQ_ROWS)
+    dq_np = dq[:, :, rows].float().cpu().numpy()
+    # the key window: its keys, and the device rows that can see them
+    keys = _window_keys(wl, seed=rank)
+    where = _block_of_positions(wl)[keys]
+    win_rows = np.nonzero(qpos >= keys.min())[0]
+    assert 0 < len(win_rows) <= KEY_WINDOW
+    dk_np = np.stack([dk[j][0, :, i].double().cpu().numpy() for j, i in where], axis=1)   # [Hkv, K, d]
+    dv_np = np.stack([dv[j][0, :, i].double().cpu().numpy() for j, i in where], axis=1)
+
+    def dq_job(g, h, sl, kh, vh):
+        r_ = rows[sl]
+        q = ring_inputs.rows(wl, "q", 0, h, qpos[r_])
+        do = ring_inputs.rows(wl, "do", 0, h, qpos[r_])
+        r = oracle.attention_backward_rows(q, qpos[r_], kh, vh, k_pos, do, True)
+        a = (np.abs(do.astype(np.float64)) * np.abs(r["out"])).sum(axis=1, keepdims=True)
+        budget = (scale * (2.0 ** -7 * a * np.abs(r["p_k"]) + 2.0 ** -8 * r["abs_ds_k"]) +
+                  2.0 ** -8 * np.abs(r["dq"]) + 1e-4)
+        got = dq_np[0, h, sl]
+        assert np.isfinite(got).all()
+        return float((np.abs(got - r["dq"]) / budget).max())
+
+    def key_job(g, h, sl, kh, vh):
+        r_ = win_rows[sl]
+        q = ring_inputs.rows(wl, "q", 0, h, qpos[r_])
+        do = ring_inputs.rows(wl, "do", 0, h, qpos[r_])
+        return g, oracle.key_gradients(q, qpos[r_], kh, vh, k_pos, do, True, keys)
+
+    from threadpoolctl import threadpool_limits
+    dq_err = 0.0
+    kg = {}
+    with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(sampling.threads()) as ex:
+        for g in range(wl.heads_kv):
+            kh = ring_inputs.head(wl, "k", 0, g)
+            vh = ring_inputs.head(wl, "v", 0, g)
+            jobs_dq, jobs_k = [], []
+            for h in range(g * group, (g + 1) * group):
+                for r0 in range(0, len(rows), 32):
+                    jobs_dq.append(ex.submit(dq_job, g, h, slice(r0, r0 + 32), kh, vh))
+                for r0 in range(0, len(win_rows), 128):
+                    jobs_k.append(ex.submit(key_job, g, h, slice(r0, r0 + 128), kh, vh))
+            for j in jobs_dq:
+                dq_err = max(dq_err, j.result())
+            for j in jobs_k:
+                gg, r = j.result()
+                acc = kg.setdefault(gg, {})
+                for key_, val in r.items():
+                    acc[key_] = acc.get(key_, 0.0) + val
+    dk_err = dv_err = 0.0
     for g in range(wl.heads_kv):
-        k = ring_inputs.head(wl, "k", 0, g)
-        v = ring_inputs.head(wl, "v", 0, g)
-        for h in range(g * group, (g + 1) * group):
-            q = ring_inputs.rows(wl, "q", 0, h, pos)
-            do = ring_inputs.rows(wl, "do", 0, h, pos)
-            r = oracle.attention_backward_rows(q, pos, k, v, k_pos, do, True)
-            a = (np.abs(do.astype(np.float64)) * np.abs(r["out"])).sum(axis=1, keepdims=True)
-            budget = (scale * (2.0 ** -7 * a * np.abs(r["p_k"]) + 2.0 ** -8 * r["abs_ds_k"]) +
-                      2.0 ** -8 * np.abs(r["dq"]) + 1e-4)
-            assert np.isfinite(dq_np[0, h]).all()
-            err = max(err, float((np.abs(dq_np[0, h] - r["dq"]) / budget).max()))
+        r = kg[g]
+        b_dk = scale * (2.0 ** -8 * r["abs_ds_q"] + 2.0 ** -7 * r["p_a_q"]) + 2.0 ** -8 * np.abs(r["dk"]) + 1e-6
+        b_dv = 2.0 ** -7 * r["p_do"] + 2.0 ** -8 * np.abs(r["dv"]) + 1e-6
+        assert np.isfinite(dk_np[g]).all() and np.isfinite(dv_np[g]).all()
+        dk_err = max(dk_err, float((np.abs(dk_np[g] - r["dk"]) / b_dk).max()))
+        dv_err = max(dv_err, float((np.abs(dv_np[g] - r["dv"]) / b_dv).max()))
+
     # Identities of one device's contribution, per KV head and column. Every
     # row's P~ sums to 1 within 2^-8 (LSE within 1e-3, bf16 rounding 2^-9),
     # so |sum dV - sum dO| <= 2^-8 sum |dO|; the dS~ of a row sum to D - D~,
@@ -186,9 +267,11 @@ def test_full_size_backward_sampled_rows_and_identities(gpu, name, rank):
     do_abs = grouped.abs().sum(dim=(2, 3))
     id_dk = float((sum_dk.abs() / abs_dk).max())
     id_dv = float(((sum_dv - do_sum).abs() / do_abs).max())
-    print(f"  {name}: dQ rows={len(rows)} x {wl.heads_q} heads: max err / budget {err:.3f}; "
+    print(f"  {name}: dQ rows={len(rows)} x {wl.heads_q} heads: max err / budget {dq_err:.3f}; "
+          f"dK/dV at {len(keys)} keys x {wl.heads_kv} KV heads ({len(win_rows)} rows see them): "
+          f"max err / budget {dk_err:.3f} / {dv_err:.3f}; "
           f"|sum dK|/sum|dK| {id_dk:.3e}; |sum dV - sum dO|/sum|dO| {id_dv:.3e}", flush=True)
-    assert err <= 1.0
+    assert dq_err <= 1.0 and dk_err <= 1.0 and dv_err <= 1.0
     assert id_dk <= 1e-2 and id_dv <= 2.0 ** -8
 
 

@@ -15,6 +15,8 @@ import ring_inputs
 import ring_attention_blockwise_amd as ra
 from ring_attention_blockwise_amd import harness
 
+import sampling
+
 pytestmark = pytest.mark.gpu
 
 TOL_O = {"f32": 1e-5, "bf16": 2e-2}
@@ -27,32 +29,14 @@ def _copy_stream():
     return torch.cuda.Stream()
 
 
-def sample_rows(wl, n_random, seed):
-    c = wl.local_len
-    base = {0, 1, 2, 31, 32, 63, 64, 65, 127, 128, 129, 255, 256, c - 129, c - 128, c - 2, c - 1}
-    if wl.partition == "zigzag":
-        g = c // 2
-        base |= {g - 2, g - 1, g, g + 1, g + 127, g + 128}
-    rng = np.random.default_rng(seed)
-    extra = rng.choice(c, size=min(n_random, c), replace=False)
-    return np.array(sorted(r for r in base | set(extra.tolist()) if 0 <= r < c), dtype=np.int64)
-
-
 def _oracle_for(wl, rank, rows):
-    """Build the share on the GPU while computing oracle rows head by head."""
+    """Build the share on the GPU while the oracle computes the chosen rows
+    on worker threads."""
     import torch
     positions = oracle.device_positions(wl.partition, wl.world, rank, wl.local_len)[rows]
-    k_pos = np.arange(wl.total_len)
-    G = wl.heads_q // wl.heads_kv
-    ref_o = np.zeros((wl.batch, wl.heads_q, len(rows), wl.head_dim))
-    ref_l = np.zeros((wl.batch, wl.heads_q, len(rows)))
-
-    def on_head(b, g, kh, vh):
-        for h in range(g * G, (g + 1) * G):
-            q = ring_inputs.rows(wl, "q", b, h, positions)
-            ref_o[b, h], ref_l[b, h] = oracle.attention_rows(q, positions, kh, vh, k_pos, wl.causal)
-
-    share = harness.build_share(wl, rank, torch.device("cuda:0"), on_head=on_head)
+    ref = sampling.OracleRows(wl, positions)
+    share = harness.build_share(wl, rank, torch.device("cuda:0"), on_head=ref.on_head)
+    ref_o, ref_l = ref.result()
     return share, ref_o, ref_l
 
 
@@ -188,17 +172,34 @@ FULL = [
 def test_full_size_workload_sampled_rows(gpu, name, rank):
     import torch
     wl = W[name]
-    rows = sample_rows(wl, 48, seed=rank)
+    tied = np.zeros(0, dtype=np.int64)
+    if wl.dup_frac > 0:
+        # rows whose best key has a visible exact twin (a tie in the row max)
+        pos_all = oracle.device_positions(wl.partition, wl.world, rank, wl.local_len)
+        tied = sampling.tied_argmax_rows(wl, pos_all, heads=range(0, wl.heads_q, 4), n_pool=2048, seed=rank)
+        print(f"{name} rank {rank}: {len(tied)} rows with a tied best key", flush=True)
+        if rank == wl.world - 1:
+            assert len(tied) >= 32
+    rows = sampling.sample_rows(wl, seed=rank, extra=tied)
+    assert len(rows) >= sampling.MIN_ROWS
     print(f"{name} rank {rank}: building share + oracle on {len(rows)} rows", flush=True)
     share, ref_o, ref_l = _oracle_for(wl, rank, rows)
     out, lse = harness.run_forward(share, copy_stream=_copy_stream())
     torch.cuda.synchronize()
     _check(out, lse, rows, ref_o, ref_l, wl.dtype)
+    if len(tied):
+        _check(out, lse, tied, *_subset(rows, tied, ref_o, ref_l), wl.dtype)
     # properties that hold for every row
     assert torch.isfinite(lse).all()
     assert torch.isfinite(out.float()).all()
     if wl.v_dist == "uniform":
         assert out.float().abs().max().item() <= 1.0
+
+
+def _subset(rows, pick, ref_o, ref_l):
+    idx = np.searchsorted(rows, pick)
+    assert np.array_equal(rows[idx], pick)
+    return ref_o[:, :, idx], ref_l[:, :, idx]
 
 
 @pytest.mark.parametrize("rank", [0, 5])
@@ -208,7 +209,8 @@ def test_full_size_striped_partition_sampled_rows(gpu, rank):
     partially masked."""
     import torch
     wl = W["striped128k_8dev_gqa"]
-    rows = sample_rows(wl, 40, seed=100 + rank)
+    rows = sampling.sample_rows(wl, seed=100 + rank)
+    assert len(rows) >= sampling.MIN_ROWS
     share, ref_o, ref_l = _oracle_for(wl, rank, rows)
     out, lse = harness.run_forward(share, copy_stream=_copy_stream())
     torch.cuda.synchronize()
