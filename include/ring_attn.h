@@ -172,8 +172,11 @@ size_t ring_attn_forward_workspace_size(const ra_ring_desc* desc);
  * Steps whose block has no key visible to any local row launch no kernel;
  * the block is still received. Step kernels never read a slot while it is
  * being filled. The two streams are ordered by four untimed hipEvent_t that
- * the library creates on first use per calling thread and device and keeps
- * until the thread ends (no other state survives a call). The copy stream
+ * the library creates on first use per calling thread and device and reuses
+ * on later calls from that thread (no other state survives a call). They are
+ * destroyed only by ring_attn_release_thread_events(); a thread that ends
+ * without calling it leaves them to the runtime, which frees them when the
+ * process exits (four events per device the thread used). The copy stream
  * forks from and joins back into compute_stream through these events, so a
  * call can be captured into a HIP graph on compute_stream (pass
  * step_events = NULL while capturing). */
@@ -322,6 +325,15 @@ int ring_attn_events_create(int32_t n, void** events);
 int ring_attn_event_elapsed_ms(void* start, void* stop, float* ms);
 int ring_attn_events_destroy(int32_t n, void* const* events);
 int ring_attn_synchronize(void* stream);
+
+/* Destroy the ordering events that ring_attn_forward and ring_attn_backward
+ * keep for the calling thread (every device it used); the next driver call on
+ * this thread creates them again. Call it before a thread that used the
+ * drivers ends, once the work it enqueued no longer needs ordering (e.g. after
+ * synchronising both streams). Makes no HIP call when the thread holds none.
+ * Returns RA_OK, or RA_ERR_HIP if a destroy fails (the rest are still
+ * destroyed). */
+int ring_attn_release_thread_events(void);
 
 /* Measurement aid (not part of the attention path): the dense bf16 matrix-core
  * rate and shader clock of this device, with the instruction the step kernels

@@ -32,7 +32,7 @@ EXPORTED = (
     "ring_attn_events_create", "ring_attn_event_elapsed_ms", "ring_attn_events_destroy",
     "ring_attn_synchronize", "ring_attn_ulysses_workspace_size", "ring_attn_ulysses_forward",
     "ring_attn_backward_prep", "ring_attn_backward_step", "ring_attn_backward_workspace_size",
-    "ring_attn_backward", "ring_attn_mfma_probe",
+    "ring_attn_backward", "ring_attn_mfma_probe", "ring_attn_release_thread_events",
 )
 
 
@@ -103,6 +103,7 @@ def lib() -> ctypes.CDLL:
             "ring_attn_event_elapsed_ms": (ctypes.c_int, [P, P, ctypes.POINTER(ctypes.c_float)]),
             "ring_attn_events_destroy": (ctypes.c_int, [I32, P]),
             "ring_attn_synchronize": (ctypes.c_int, [P]),
+            "ring_attn_release_thread_events": (ctypes.c_int, []),
             "ring_attn_mfma_probe": (ctypes.c_int, [I32, I32, P, P, P]),
             "ring_attn_ulysses_workspace_size": (SZ, [UD]),
             "ring_attn_ulysses_forward": (ctypes.c_int, [UD, P, P, P, P, P, P, SZ, P]),
@@ -419,6 +420,12 @@ class StepEvents:
 
 def synchronize(stream=None):
     _check(lib().ring_attn_synchronize(_stream(stream)), "synchronize")
+
+
+def release_thread_events():
+    """Destroy the drivers' cached ordering events of the calling thread
+    (ring_attn_release_thread_events); later driver calls recreate them."""
+    _check(lib().ring_attn_release_thread_events(), "release_thread_events")
 
 
 def mfma_probe(blocks: int, iters: int, sink, stamps, stream=None):

@@ -357,11 +357,11 @@ size_t ring_attn_forward_workspace_size(const ra_ring_desc* d) {
 
 namespace {
 
-// Per-thread cache of the driver's synchronisation events (never timed).
-// The forward driver's ordering events: one untimed set per calling thread
-// and device, created on first use and kept for the life of the thread. A
-// thread enqueues one forward completely before the next, and a stream wait
-// binds to the record made just before it, so reusing the set is safe.
+// Per-thread cache of the drivers' ordering events (never timed): one set per
+// calling thread and device, created on first use and reused until
+// ring_attn_release_thread_events() destroys them. A thread enqueues one
+// driver call completely before the next, and a stream wait binds to the
+// record made just before it, so reusing the set is safe.
 struct DriverEvents {
   bool created = false;
   hipEvent_t ready[2] = {nullptr, nullptr};  // slot filled (copy stream)
@@ -949,6 +949,21 @@ int ring_attn_events_destroy(int32_t n, void* const* events) {
   for (int i = 0; i < n; ++i)
     if (events[i]) (void)hipEventDestroy(static_cast<hipEvent_t>(events[i]));
   return RA_OK;
+}
+
+int ring_attn_release_thread_events(void) {
+  hipError_t first = hipSuccess;
+  for (DriverEvents& ev : g_events) {
+    if (!ev.created) continue;
+    for (int i = 0; i < 2; ++i) {
+      const hipError_t a = hipEventDestroy(ev.ready[i]);
+      const hipError_t b = hipEventDestroy(ev.freed[i]);
+      if (first == hipSuccess) first = a != hipSuccess ? a : b;
+      ev.ready[i] = ev.freed[i] = nullptr;
+    }
+    ev.created = false;
+  }
+  return first == hipSuccess ? RA_OK : hip_fail(first, "hipEventDestroy");
 }
 
 int ring_attn_synchronize(void* stream) {

@@ -12,13 +12,13 @@
 // Two kernels, both v_mfma_f32_32x32x16_bf16:
 //  * bwd_dq_kernel: query-stationary like the forward step. 8 waves x 32
 //    rows; Q^T and dO^T stay in VGPRs; K and V tiles of 64 keys go HBM -> LDS
-//    by buffer-to-LDS copies into three stages. Per tile: S^T = K Q^T and
+//    by buffer-to-LDS copies into four stages. Per tile: S^T = K Q^T and
 //    dP^T = V dO^T (K, V read row-wise), dS^T in registers (one row per
 //    lane, so LSE and D are one value per lane), then dQ^T += K^T dS^T with
 //    K^T read by ds_read_b64_tr_b16 and dS^T (bf16) as the B operand.
 //  * bwd_dkdv_kernel: key-stationary. 4 waves x 32 keys, one wave per SIMD;
 //    K^T and V^T stay in VGPRs; tiles of 64 query rows of Q, dO and the two
-//    row terms are copied into three LDS stages, for every query head of the
+//    row terms are copied into four LDS stages, for every query head of the
 //    GQA group. Per tile: S = Q K^T and dP = dO V^T with the accumulators
 //    started at -LSE/scale and -D (so no per-element subtraction), P and dS
 //    in registers (one key per lane), then dV^T += dO^T P and

@@ -260,3 +260,9 @@ def test_total_rows_beyond_the_grid_limit_are_rejected():
     assert L.ring_attn_visible_pairs(ctypes.byref(ok)) == (1 << 12) * (1 << 12)
     rd = ra.ring_desc(1 << 13, 1 << 10, 1 << 10, 128, 1 << 12, 8, 0, partition="contiguous")
     assert L.ring_attn_forward_workspace_size(ctypes.byref(rd)) == 0
+
+
+def test_release_thread_events_without_events_makes_no_hip_call():
+    """A thread that never ran a driver holds no events: the release returns
+    OK without touching the (absent) GPU."""
+    assert ra.lib().ring_attn_release_thread_events() == ra.OK

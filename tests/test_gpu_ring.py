@@ -120,6 +120,22 @@ def test_determinism(gpu):
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
+def test_release_thread_events_then_forward_again(gpu):
+    """Destroying the drivers' cached events changes nothing: the next call
+    creates them again and gives the same bits."""
+    import torch
+    wl = W["zigzag8k_8dev_d128"]
+    share = harness.build_share(wl, 1, gpu)
+    cs = _copy_stream()
+    a = [x.clone() for x in harness.run_forward(share, copy_stream=cs)]
+    torch.cuda.synchronize()
+    ra.release_thread_events()
+    ra.release_thread_events()  # nothing left to destroy
+    b = harness.run_forward(share, copy_stream=cs)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
 def test_partitions_agree_per_global_row(gpu):
     """Contiguous, zigzag and striped rings give the same rows (by global position)."""
     import torch
