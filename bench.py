@@ -46,8 +46,29 @@ def effective_flops(wl, pairs):
     return [4.0 * wl.head_dim * wl.heads_q * wl.batch * p for p in pairs]
 
 
-def cpu_baseline(wl, rank, budget_s=12.0):
-    """Time the float64 CPU oracle on a bounded sample of the same share."""
+def host_info():
+    """The host CPU the oracle runs on: model name, logical CPUs and the BLAS
+    thread count its matrix products use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        blas = None
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "blas_threads": blas}
+
+
+def cpu_baseline(wl, rank, share_flops, budget_s=12.0):
+    """Time the float64 CPU oracle on a bounded sample of the same share, and
+    extrapolate its rate to the whole share (labelled as extrapolated)."""
     import oracle
     import ring_inputs
     positions = oracle.device_positions(wl.partition, wl.world, rank, wl.local_len)
@@ -75,19 +96,20 @@ def cpu_baseline(wl, rank, budget_s=12.0):
         rows_done += n_rows
         heads_done = G
         n_rows *= 2
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    host = host_info()
+    rate = flops / spent
     return {
-        "value": flops / spent / 1e12,
+        "value": rate / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        "cores": int(host["blas_threads"] or os.cpu_count() or 1),
         "kind": "oracle",
         "sample": f"{rows_done} query rows of device {rank} x {heads_done} query heads (one KV group), "
                   f"float64 full softmax over all {wl.total_len} global keys, {spent:.1f} s of CPU time; "
-                  f"effective FLOPs counted as for the GPU",
+                  f"effective FLOPs counted as for the GPU; 'cores' is the BLAS thread count (the "
+                  f"elementwise passes run on one thread)",
+        **host,
+        "full_share_s_extrapolated": round(share_flops / rate, 1),
+        "extrapolation": "whole share's effective FLOPs / the sample's rate (not measured)",
     }
 
 
@@ -115,7 +137,8 @@ def cpu_baseline_full(wl, rank):
                     oracle.attention_rows(q, positions, kh, vh, k_pos, wl.causal)
         return time.perf_counter() - t0
 
-    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    host = host_info()
+    threads = host["blas_threads"] or 1
     t_all = run()
     with threadpool_limits(limits=1, user_api="blas"):
         t_one = run()
@@ -124,6 +147,8 @@ def cpu_baseline_full(wl, rank):
     return {
         "value": flops / t_all / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
         "sample": f"{what}, {t_all:.2f} s",
+        **host,
+        "full_share_s": round(t_all, 3),
         "single_thread": {"value": flops / t_one / 1e12, "unit": "TFLOP/s", "cores": 1, "seconds": round(t_one, 3)},
     }
 
@@ -494,7 +519,7 @@ def main():
             cpu = cpu_baseline_full(wl, rank)
         else:
             log("timing the CPU oracle on a bounded sample")
-            cpu = cpu_baseline(wl, rank)
+            cpu = cpu_baseline(wl, rank, total_flops)
 
     rec = {
         "metric": "effective causal attention TFLOP/s per ring step at 1 GPU; % of bf16 MFMA peak",

@@ -36,3 +36,12 @@ def test_zigzag_ring_is_exactly_balanced(name):
     lb = bench.load_balance(wl)
     assert lb["pairs_max"] == lb["pairs_min"] == L * (L + 1) // 2 // wl.world
     assert lb["max_over_mean"] == 1.0 and lb["min_over_mean"] == 1.0
+
+
+def test_cpu_baseline_reports_host_and_extrapolation():
+    wl = ring_inputs.WORKLOADS["zigzag8k_8dev_d128"]
+    rec = bench.cpu_baseline(wl, 0, share_flops=1.0e12, budget_s=0.2)
+    assert rec["kind"] == "oracle" and rec["unit"] == "TFLOP/s" and rec["value"] > 0
+    assert rec["os_cpu_count"] == os.cpu_count() and rec["cores"] >= 1
+    assert "cpu_model" in rec and rec["blas_threads"] is not None
+    assert rec["full_share_s_extrapolated"] == pytest.approx(1.0 / rec["value"], rel=1e-2)
