@@ -185,6 +185,32 @@ int ring_attn_forward(const ra_ring_desc* desc, const void* q_local,
                       void* out, float* lse, void* workspace, size_t workspace_bytes,
                       void* compute_stream, void* copy_stream, void* const* step_events);
 
+/* ---- forward without device allocation ------------------------------------ */
+
+/* For callers that cannot allocate device memory or hand over a workspace:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same ring and same kernels as ring_attn_forward with
+ * copy_stream = NULL (bit for bit the same out and lse): every receive copy
+ * and step runs in order on `stream`. The receive slots and the running
+ * state live in a device array owned by the library, RA_NOALLOC_SCRATCH_BYTES
+ * long, one per GPU, held from the time the library's code is loaded on that
+ * GPU until the process ends. The call allocates nothing (no hipMalloc,
+ * hipFree, event or stream creation); the first call on a device looks up
+ * that device's array address once.
+ *   desc, q_local, k_blocks, v_blocks, out, lse   as ring_attn_forward.
+ *   stream         hipStream_t (NULL: the default stream).
+ * Errors: as ring_attn_forward; RA_ERR_WORKSPACE when the share needs more
+ * than RA_NOALLOC_SCRATCH_BYTES (ring_attn_forward_workspace_size(desc) - 256
+ * bytes), with nothing enqueued. Every call on a GPU uses that GPU's one
+ * array and leaves its contents behind (nothing in it has to start at zero:
+ * the first step of a ring ignores the old state): calls that overlap on one
+ * GPU (on different streams or from different threads) race on it, so order
+ * them, e.g. on one stream. */
+#define RA_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+int ring_attn_forward_noalloc(const ra_ring_desc* desc, const void* q_local,
+                              const void* const* k_blocks, const void* const* v_blocks,
+                              void* out, float* lse, void* stream);
+
 /* ---- Ulysses: sequence <-> head all-to-all around local attention --------- */
 
 /* One device's share of DeepSpeed-Ulysses ([L30] section 3.3, and the

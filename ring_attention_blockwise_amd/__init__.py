@@ -33,6 +33,7 @@ EXPORTED = (
     "ring_attn_synchronize", "ring_attn_ulysses_workspace_size", "ring_attn_ulysses_forward",
     "ring_attn_backward_prep", "ring_attn_backward_step", "ring_attn_backward_workspace_size",
     "ring_attn_backward", "ring_attn_mfma_probe", "ring_attn_release_thread_events",
+    "ring_attn_forward_noalloc",
 )
 
 
@@ -93,6 +94,7 @@ def lib() -> ctypes.CDLL:
             "ring_attn_finalize": (ctypes.c_int, [SD, P, P, P, P, P, P]),
             "ring_attn_forward_workspace_size": (SZ, [RD]),
             "ring_attn_forward": (ctypes.c_int, [RD, P, P, P, P, P, P, SZ, P, P, P]),
+            "ring_attn_forward_noalloc": (ctypes.c_int, [RD, P, P, P, P, P, P]),
             "ring_attn_partition_segments": (ctypes.c_int, [I32, I32, I32, I64, ctypes.POINTER(Segment),
                                                             ctypes.POINTER(I32)]),
             "ring_attn_ring_step_desc": (ctypes.c_int, [RD, I32, SD, ctypes.POINTER(I32)]),
@@ -280,6 +282,25 @@ def forward(rd: RingDesc, q_local, k_blocks: Sequence, v_blocks: Sequence, out, 
         _ptr(out, dt, (B, Hq, c, D), "out"), _ptr(lse, torch.float32, (B, Hq, c), "lse"),
         ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(compute_stream),
         None if copy_stream is None else ctypes.c_void_p(copy_stream.cuda_stream), ev), "ring_attn_forward")
+
+
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024  # RA_NOALLOC_SCRATCH_BYTES
+
+
+def forward_noalloc(rd: RingDesc, q_local, k_blocks: Sequence, v_blocks: Sequence, out, lse, stream=None):
+    """One device's whole ring without a workspace (ring_attn_forward_noalloc):
+    the library's per-GPU scratch array holds the receive slots and state."""
+    torch = _torch()
+    dt = _dtype_of(rd.dtype)
+    B, Hq, Hk, D, c, n = rd.batch, rd.heads_q, rd.heads_kv, rd.head_dim, rd.local_len, rd.world
+    if len(k_blocks) != n or len(v_blocks) != n:
+        raise ValueError(f"need {n} K and V blocks")
+    kp = (ctypes.c_void_p * n)(*[_ptr(k, dt, (B, Hk, c, D), f"k_blocks[{i}]").value for i, k in enumerate(k_blocks)])
+    vp = (ctypes.c_void_p * n)(*[_ptr(v, dt, (B, Hk, c, D), f"v_blocks[{i}]").value for i, v in enumerate(v_blocks)])
+    _check(lib().ring_attn_forward_noalloc(
+        ctypes.byref(rd), _ptr(q_local, dt, (B, Hq, c, D), "q_local"), kp, vp,
+        _ptr(out, dt, (B, Hq, c, D), "out"), _ptr(lse, torch.float32, (B, Hq, c), "lse"), _stream(stream)),
+        "ring_attn_forward_noalloc")
 
 
 def ulysses_desc(batch, heads_q, heads_kv, head_dim, seq_len, world, rank, dtype=BF16, causal=True,

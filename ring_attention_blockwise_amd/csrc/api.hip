@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "backward.h"
@@ -389,9 +390,11 @@ hipError_t driver_events(DriverEvents** out) {
 
 }  // namespace
 
-int ring_attn_forward(const ra_ring_desc* d, const void* q_local, const void* const* k_blocks,
-                      const void* const* v_blocks, void* out, float* lse, void* workspace, size_t workspace_bytes,
-                      void* compute_stream, void* copy_stream, void* const* step_events) {
+namespace {
+
+// Arguments every forward entry point checks before anything is enqueued.
+int check_forward_args(const ra_ring_desc* d, const void* q_local, const void* const* k_blocks,
+                       const void* const* v_blocks, const void* out, void* const* step_events) {
   int rc = check_ring_desc(d);
   if (rc) return rc;
   const int n = d->world;
@@ -409,14 +412,17 @@ int ring_attn_forward(const ra_ring_desc* d, const void* q_local, const void* co
   if (step_events)
     for (int i = 0; i < 2 * n; ++i)
       if (!step_events[i]) return fail(RA_ERR_INVALID_ARG, "step_events[%d] is NULL", i);
-  RingLayout L;
-  ring_layout(d, &L);
-  if (workspace == nullptr || workspace_bytes < L.total)
-    return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, workspace_bytes);
-  if (copy_stream != nullptr && copy_stream == compute_stream)
-    return fail(RA_ERR_INVALID_ARG, "copy_stream must differ from compute_stream (or be NULL)");
-  if (!has_rows) return RA_OK;
+  return RA_OK;
+}
 
+// The ring of one device, after validation: `base` is the 256-byte aligned
+// start of a workspace laid out by ring_layout. With xs == cs every receive
+// copy runs on the compute stream and no event is created or recorded.
+int forward_run(const ra_ring_desc* d, const RingLayout& L, const void* q_local, const void* const* k_blocks,
+                const void* const* v_blocks, void* out, float* lse, char* base, hipStream_t cs, hipStream_t xs,
+                void* const* step_events) {
+  const int n = d->world;
+  int rc;
   // Plan the steps on the host: descriptors and which launch.
   std::vector<ra_step_desc> steps(n);
   std::vector<int32_t> owner(n);
@@ -432,25 +438,24 @@ int ring_attn_forward(const ra_ring_desc* d, const void* q_local, const void* co
     }
   }
 
-  char* base = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~(uintptr_t)255);
   void* slot_k[2] = {base + L.off_slot[0][0], base + L.off_slot[1][0]};
   void* slot_v[2] = {base + L.off_slot[0][1], base + L.off_slot[1][1]};
   float* o = reinterpret_cast<float*>(base + L.off_o);
   float* m = reinterpret_cast<float*>(base + L.off_m);
   float* l = reinterpret_cast<float*>(base + L.off_l);
 
-  hipStream_t cs = static_cast<hipStream_t>(compute_stream);
-  hipStream_t xs = copy_stream ? static_cast<hipStream_t>(copy_stream) : cs;
+  const bool two_streams = xs != cs;
   DriverEvents* ev = nullptr;
-  hipError_t e = driver_events(&ev);
-  if (e != hipSuccess) return hip_fail(e, "event creation");
+  hipError_t e;
+  if (two_streams)
+    if ((e = driver_events(&ev)) != hipSuccess) return hip_fail(e, "event creation");
   bool freed_recorded[2] = {false, false};
 
   // The copy stream must not start before work already queued on the compute
   // stream that produced the inputs: order it after the compute stream once
   // (only when something will be copied, so that a captured call leaves no
   // branch of the copy stream unjoined).
-  if (xs != cs && n > 1) {
+  if (two_streams && n > 1) {
     if ((e = hipEventRecord(ev->freed[0], cs)) != hipSuccess) return hip_fail(e, "event record");
     if ((e = hipStreamWaitEvent(xs, ev->freed[0], 0)) != hipSuccess) return hip_fail(e, "stream wait");
   }
@@ -459,7 +464,7 @@ int ring_attn_forward(const ra_ring_desc* d, const void* q_local, const void* co
     // step s reads slot s%2; it was last read by step s-2
     const int slot = s & 1;
     hipError_t err;
-    if (freed_recorded[slot] && xs != cs)
+    if (freed_recorded[slot] && two_streams)
       if ((err = hipStreamWaitEvent(xs, ev->freed[slot], 0)) != hipSuccess) return err;
     if ((err = hipMemcpyAsync(slot_k[slot], k_blocks[owner[s]], L.block_bytes, hipMemcpyDeviceToDevice, xs)) !=
         hipSuccess)
@@ -467,7 +472,7 @@ int ring_attn_forward(const ra_ring_desc* d, const void* q_local, const void* co
     if ((err = hipMemcpyAsync(slot_v[slot], v_blocks[owner[s]], L.block_bytes, hipMemcpyDeviceToDevice, xs)) !=
         hipSuccess)
       return err;
-    return hipEventRecord(ev->ready[slot], xs);
+    return two_streams ? hipEventRecord(ev->ready[slot], xs) : hipSuccess;
   };
 
   for (int s = 0; s < n; ++s) {
@@ -479,7 +484,7 @@ int ring_attn_forward(const ra_ring_desc* d, const void* q_local, const void* co
     if (s > 0) {
       kb = slot_k[s & 1];
       vb = slot_v[s & 1];
-      if (xs != cs)
+      if (two_streams)
         if ((e = hipStreamWaitEvent(cs, ev->ready[s & 1], 0)) != hipSuccess) return hip_fail(e, "stream wait");
     }
     if (step_events)
@@ -502,7 +507,7 @@ int ring_attn_forward(const ra_ring_desc* d, const void* q_local, const void* co
     if (step_events)
       if ((e = hipEventRecord(static_cast<hipEvent_t>(step_events[2 * s + 1]), cs)) != hipSuccess)
         return hip_fail(e, "step event");
-    if (s > 0 && xs != cs) {
+    if (s > 0 && two_streams) {
       if ((e = hipEventRecord(ev->freed[s & 1], cs)) != hipSuccess) return hip_fail(e, "event record");
       freed_recorded[s & 1] = true;
     }
@@ -518,6 +523,71 @@ int ring_attn_forward(const ra_ring_desc* d, const void* q_local, const void* co
   // The copy stream's last work is ordered before the compute stream's last
   // step (which waited on it), so the caller only needs to sync compute_stream.
   return RA_OK;
+}
+
+// Scratch of ring_attn_forward_noalloc: receive slots and state live in this
+// file-scope device array instead of a caller's workspace. Each device holds
+// its own copy (at its own address) from the time the library's code is
+// loaded there until the process ends. In host code `scratch` only names the
+// symbol; its device address comes from hipGetSymbolAddress, looked up once
+// per device with that device current and kept in g_scratch_addr.
+constexpr size_t kScratchBytes = (size_t)RA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & 255) != 0) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+int ring_attn_forward(const ra_ring_desc* d, const void* q_local, const void* const* k_blocks,
+                      const void* const* v_blocks, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                      void* compute_stream, void* copy_stream, void* const* step_events) {
+  int rc = check_forward_args(d, q_local, k_blocks, v_blocks, out, step_events);
+  if (rc) return rc;
+  RingLayout L;
+  ring_layout(d, &L);
+  if (workspace == nullptr || workspace_bytes < L.total)
+    return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, workspace_bytes);
+  if (copy_stream != nullptr && copy_stream == compute_stream)
+    return fail(RA_ERR_INVALID_ARG, "copy_stream must differ from compute_stream (or be NULL)");
+  if (!(d->local_len > 0 && d->batch > 0)) return RA_OK;
+  char* base = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~(uintptr_t)255);
+  hipStream_t cs = static_cast<hipStream_t>(compute_stream);
+  hipStream_t xs = copy_stream ? static_cast<hipStream_t>(copy_stream) : cs;
+  return forward_run(d, L, q_local, k_blocks, v_blocks, out, lse, base, cs, xs, step_events);
+}
+
+int ring_attn_forward_noalloc(const ra_ring_desc* d, const void* q_local, const void* const* k_blocks,
+                              const void* const* v_blocks, void* out, float* lse, void* stream) {
+  int rc = check_forward_args(d, q_local, k_blocks, v_blocks, out, nullptr);
+  if (rc) return rc;
+  RingLayout L;
+  ring_layout(d, &L);
+  const size_t need = L.total - 256;  // the scratch is already 256-byte aligned
+  if (need > kScratchBytes)
+    return fail(RA_ERR_WORKSPACE, "share needs %zu bytes of scratch, the no-allocation forward has %zu", need,
+                kScratchBytes);
+  if (!(d->local_len > 0 && d->batch > 0)) return RA_OK;
+  void* base = nullptr;
+  const hipError_t e = scratch_address(&base);
+  if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+  hipStream_t cs = static_cast<hipStream_t>(stream);
+  return forward_run(d, L, q_local, k_blocks, v_blocks, out, lse, static_cast<char*>(base), cs, cs, nullptr);
 }
 
 namespace {

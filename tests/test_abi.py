@@ -266,3 +266,23 @@ def test_release_thread_events_without_events_makes_no_hip_call():
     """A thread that never ran a driver holds no events: the release returns
     OK without touching the (absent) GPU."""
     assert ra.lib().ring_attn_release_thread_events() == ra.OK
+
+
+def test_forward_noalloc_rejects_before_any_gpu_work():
+    """Shares past the scratch size, bad descriptors and NULL blocks are
+    rejected on the host (fake pointers: nothing may be touched)."""
+    L = ra.lib()
+    blocks = (ctypes.c_void_p * 4)(*([0x10000] * 4))
+    ok = ra.ring_desc(1, 2, 1, 64, 16, 4, 0)
+    assert ra.forward_workspace_size(ok) - 256 <= ra.NOALLOC_SCRATCH_BYTES
+    # 128K/8 GQA share: two K/V receive slots and the fp32 state are ~1 GB
+    big = ra.ring_desc(1, 32, 8, 128, 16384, 8, 0, partition="zigzag")
+    assert ra.forward_workspace_size(big) - 256 > ra.NOALLOC_SCRATCH_BYTES
+    blocks8 = (ctypes.c_void_p * 8)(*([0x10000] * 8))
+    assert L.ring_attn_forward_noalloc(ctypes.byref(big), FAKE, blocks8, blocks8, FAKE, FAKE, None) == ra.ERR_WORKSPACE
+    assert "scratch" in ra.last_error()
+    bad = ra.ring_desc(1, 2, 1, 64, 15, 4, 0, partition="zigzag")   # odd local length
+    assert L.ring_attn_forward_noalloc(ctypes.byref(bad), FAKE, blocks, blocks, FAKE, FAKE, None) == ra.ERR_INVALID_ARG
+    nulls = (ctypes.c_void_p * 4)(*([0x10000] * 3 + [None]))
+    assert L.ring_attn_forward_noalloc(ctypes.byref(ok), FAKE, blocks, nulls, FAKE, FAKE, None) == ra.ERR_INVALID_ARG
+    assert L.ring_attn_forward_noalloc(None, FAKE, blocks, blocks, FAKE, FAKE, None) == ra.ERR_INVALID_ARG
