@@ -1,4 +1,4 @@
-// bf16 ring step on the CDNA4 matrix cores (gfx950).
+// bf16 ring step on the CDNA4 matrix cores (gfx950), software-pipelined.
 //
 // One launch folds one K/V block into the running (O, m, l) state of the local
 // query block — the block step of "distributed training hands-on code",
@@ -8,33 +8,30 @@
 //
 // Mapping (head_dim D in {64, 128}):
 //  * A workgroup of 8 waves owns 256 query rows of one (batch, q head); each
-//    wave owns 32 rows. Waves w and w+4 run on the same SIMD. The two groups
-//    (waves 0-3 and 4-7) run one phase apart: in each tile interval group 0
-//    issues its matrix instructions (P V of tile t-1 and S of tile t) and
-//    then runs its softmax, group 1 the other way round, so while one wave of
-//    a SIMD keeps the MFMA pipe busy its partner works on the vector ALUs
-//    ("ping-pong"). The groups meet at a workgroup barrier once per tile,
-//    where the next tile is published.
-//  * Keys are consumed in tiles of 64. K and V tiles are copied HBM -> LDS by
-//    16-byte buffer-to-LDS loads (bounds-checked by the buffer resource: rows
-//    past the block read as zero and are masked), in a ring of four LDS
-//    stages: a tile is requested four phases before its first use.
-//  * The 16-byte units of each LDS row are XOR-swizzled through the global
-//    offset, so the K reads (16 lanes x 16 B over 16 rows) and the V
-//    transposed reads (4 rows x 4 units per half-wave) are free of bank
-//    conflicts.
-//  * Scores are computed transposed, S^T = K Q^T, with
-//    v_mfma_f32_32x32x16_bf16: K (A operand) is read with ds_read_b128, Q^T
-//    (B operand) sits in VGPRs for the whole launch. In the accumulator every
-//    lane holds 32 keys of ONE query row, so row max and row sum are
-//    lane-local plus one v_permlane32_swap with the partner lane.
-//  * P^T is converted to bf16 in registers and is directly the B operand of
-//    O^T += V^T P^T: the 32x32 accumulator layout puts keys {0-3, 8-11}+4h of
-//    each 16-key chunk in lane half h, and V^T (A operand) is fetched in the
-//    same key order by ds_read_b64_tr_b16 from row-major V.
-//  * Softmax runs in base 2 with scale*log2(e) folded into one FMA per score.
-//    The reference maximum is raised lazily (only when a row's maximum grows
-//    by more than 8 in base-2 units); O and l are rescaled only then.
+//    wave owns 32 rows; two waves share each SIMD.
+//  * Keys are consumed in tiles of 64. Every wave runs the same pipeline: in
+//    iteration t it issues, interleaved in one instruction stream, the
+//    matrix-core products O^T += V^T P^T of tile t-1 and S^T = K Q^T of tile
+//    t+1, and the vector work of tile t (row maximum, exponentials, row sum,
+//    bf16 packing of P). The products never wait for the vector work of the
+//    same iteration, so the matrix pipe and the vector ALU of a SIMD run side
+//    by side in both of its waves.
+//  * The exponentials of tile t are taken against the current reference
+//    maximum before the tile's maximum is known. The reference is raised only
+//    when a row's maximum passes it by more than 8 in base-2 units (so every
+//    weight stays <= 2^8); in that rare case (always on a row's first tile)
+//    the tile's weights are recomputed against the new reference and O, l
+//    are rescaled, off the main path.
+//  * K and V tiles are copied HBM -> LDS by 16-byte buffer-to-LDS loads into
+//    two rings of four stages each: K of tile t+3 at the start of iteration
+//    t, V of tile t+2 in its middle (every wave copies one eighth of each),
+//    so a copy has about two iterations to land. One workgroup barrier per
+//    iteration publishes K of tile t+2 and V of tile t. Each copy goes to a
+//    stage whose last reader ran before the previous barrier (K of tile t is
+//    read by the products of iteration t-1 and by the rare path of iteration
+//    t).
+//  * LDS layout, swizzle, operand lane layouts and the transposed V reads are
+//    those of bf16_tiles.h.
 #include <type_traits>
 
 #include "bf16_tiles.h"
@@ -44,125 +41,117 @@ namespace {
 
 using namespace bf16k;
 
-constexpr int kWaves = 8;               // two groups of four; w and w+4 share a SIMD
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kBM = kWaves * 32;        // query rows per workgroup
-constexpr int kPrefetch = kStages - 2;  // tiles fetched ahead of the one in use
-static_assert(kStages == 4, "the copy schedule below assumes four stages");
-// 1 KB copies per wave, per tensor and half tile
-template <int D>
-constexpr int kLoadsPerWave = Layout<D>::kTileBytes / 1024 / kWaves;
-#ifndef RA_LOOKAHEAD
-#define RA_LOOKAHEAD 6
+constexpr int kBM = kWaves * 32;  // query rows per workgroup
+static_assert(kStages == 4, "the K/V rings below have four stages each");
+constexpr int kKAhead = 3;        // K of tile t + kKAhead is requested at the start of iteration t
+constexpr int kVAhead = 2;        // V of tile t + kVAhead is requested in the middle of iteration t
+
+#ifndef RA_PIPE_AHEAD
+#define RA_PIPE_AHEAD 3
 #endif
-constexpr int kLookahead = RA_LOOKAHEAD;  // MFMAs whose LDS operands are in flight
-#ifndef RA_PVS_AHEAD
-#define RA_PVS_AHEAD 4
-#endif
-constexpr int kPvsAhead = RA_PVS_AHEAD;  // same, for the interleaved P-V / S phase
-#ifndef RA_VPRE
-#define RA_VPRE 2
-#endif
-// P-V MFMAs of a matrix phase whose V^T operands are read at the end of the
-// wave's preceding softmax phase, before the barrier (the stage holding that
-// V tile was published two phases earlier and is not refilled until later).
-constexpr int kVPre = RA_VPRE;
+constexpr int kAhead = RA_PIPE_AHEAD;  // MFMAs whose LDS operands are in flight
 
-// Copy the K and V tile of 64 rows starting at local key `start` into one LDS
-// stage. The buffer resources bound the reads to the rows the block has: rows
-// past kv_len read as zero (their scores are masked).
-// One half of a tile: `half` picks the first or second half of the tile's 1 KB
-// blocks, `slot` (0..3) this wave's quarter of that half.
+// 1 KB copies per wave for one K (or V) tile
 template <int D>
-__device__ __forceinline__ void issue_tile(const char* kg, const char* vg, int64_t kv_len, int32_t start,
-                                           uint32_t k_dst, uint32_t v_dst, int half, int slot, int lane) {
+constexpr int kCopies = Layout<D>::kTileBytes / 1024 / kWaves;
+
+// Copies of one tensor (K or V) of one head into the LDS rings. Set up once
+// per work item: the head's base address in SGPRs and this lane's byte
+// offsets for the wave's kCopies 1 KB blocks of a tile (block i > 0 is
+// reached through the instruction offset i * 1024, which moves the global and
+// the LDS address alike, so one M0 value serves all of them).
+template <int D, bool IS_V>
+struct TileCopier {
   using Ly = Layout<D>;
-  const int64_t left = kv_len - start;
-  const int nbytes = (int)((left < kBN ? left : kBN) * Ly::kRowBytes);
-  const i32x4 rk = buffer_resource(kg + (int64_t)start * Ly::kRowBytes, nbytes);
-  const i32x4 rv = buffer_resource(vg + (int64_t)start * Ly::kRowBytes, nbytes);
+  uint32_t base_lo, base_hi;
+  int voff[kCopies<D>];
+
+  __device__ __forceinline__ void init(const char* g, int wave, int lane) {
+    const uint64_t p = reinterpret_cast<uint64_t>(g);
+    base_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+    base_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
 #pragma unroll
-  for (int i = 0; i < kLoadsPerWave<D>; ++i) {
-    // lane fills stored unit p of row r and fetches logical unit p ^ swz(r)
-    const int b = half * (Ly::kTileBytes / 2048) + slot * kLoadsPerWave<D> + i;  // 1 KB block of the tile
-    const int u = b * 64 + lane;
-    const int r = u / Ly::kUnits;
-    const int p = u % Ly::kUnits;
-    const uint32_t blk = (uint32_t)(b * 1024);
-    dma16(rk, k_dst + blk, r * Ly::kRowBytes + ((p ^ Ly::k_swz(r)) << 4));
-    dma16(rv, v_dst + blk, r * Ly::kRowBytes + ((p ^ Ly::v_swz(r)) << 4));
+    for (int i = 0; i < kCopies<D>; ++i) {
+      // lane fills stored unit q of row r and fetches logical unit q ^ swz(r)
+      const int b = wave * kCopies<D> + i;  // 1 KB block of the tile
+      const int u = b * 64 + lane;
+      const int r = u / Ly::kUnits;
+      const int q = u % Ly::kUnits;
+      const int swz = IS_V ? Ly::v_swz(r) : Ly::k_swz(r);
+      voff[i] = r * Ly::kRowBytes + ((q ^ swz) << 4) - i * 1024;
+    }
   }
-}
 
-// Scheduling shape of a block of N MFMAs that each take R LDS reads: the
-// reads run four MFMAs ahead of their use (enough to cover LDS latency)
-// instead of all being hoisted up front, which would exhaust the registers.
-template <int N, int R, int AHEAD>
-__device__ __forceinline__ void pipeline_lds_mfma() {
-  if constexpr (AHEAD <= 0) return;  // leave the order to the compiler
-  constexpr int kAhead = AHEAD < N ? AHEAD : N - 1;
-  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kAhead * R, 0);
-#pragma unroll
-  for (int i = 0; i < N - kAhead; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, R, 0);
+  // This wave's blocks of the tile of 64 rows starting at local row `start`
+  // into the LDS stage at `stage`. The buffer resource bounds the reads to
+  // the rows the block has: rows past kv_len read as zero. A tile past the
+  // last one (`exists` false) reads an empty range and fills its stage with
+  // zeros, which keeps the number of copies per iteration fixed (the stage it
+  // lands in is not read again).
+  __device__ __forceinline__ void copy(int64_t kv_len, int32_t start, bool exists, uint32_t stage, int wave) const {
+    const int32_t left = exists ? (int32_t)kv_len - start : 0;  // row counts are < 2^31
+    const int nbytes = (left < kBN ? left : kBN) * Ly::kRowBytes;
+    const uint64_t base = (((uint64_t)base_hi << 32) | base_lo) + (exists ? (uint64_t)start * Ly::kRowBytes : 0);
+    i32x4 rs;
+    rs[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)base);
+    rs[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32));  // stride 0
+    rs[2] = __builtin_amdgcn_readfirstlane(nbytes);
+    rs[3] = kBufferWord3;
+    const uint32_t m0 = stage + (uint32_t)(wave * kCopies<D> * 1024);
+    static_assert(kCopies<D> == 1 || kCopies<D> == 2, "one or two 1 KB blocks per wave");
+    // M0 holds the LDS destination of the copies; it is declared clobbered
+    // (nothing else in these kernels keeps a value in it).
+    if constexpr (kCopies<D> == 2)
+      asm volatile(
+          "s_mov_b32 m0, %0\n\t"
+          "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+          "buffer_load_dwordx4 %3, %2, 0 offen offset:1024 lds"
+          :
+          : "s"(m0), "v"(voff[0]), "s"(rs), "v"(voff[kCopies<D> - 1])
+          : "memory", "m0");
+    else
+      asm volatile(
+          "s_mov_b32 m0, %0\n\t"
+          "buffer_load_dwordx4 %1, %2, 0 offen lds"
+          :
+          : "s"(m0), "v"(voff[0]), "s"(rs)
+          : "memory", "m0");
   }
-  __builtin_amdgcn_sched_group_barrier(kSchedMfma, kAhead, 0);
-}
+};
 
-template <int D>
-__device__ __forceinline__ void pv_mfma(int i, const bf16x8& vt, const bf16x8 (&pf)[2][2], f32x16* oacc) {
-  using Ly = Layout<D>;
-  const int db = i % Ly::kDBlocks;
-  const int kc = i / Ly::kDBlocks;
-  oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, pf[kc / 2][kc % 2], oacc[db], 0, 0, 0);
+// Product k of an iteration in the order P-V 0 .. P-V kPre-1, then S 0,
+// P-V kPre, S 1, P-V kPre+1, ..., then whatever kind is left: is it a P-V
+// product, and its index within its kind. The operands of the first kPre
+// P-V products are read before the barrier that opens the iteration (their
+// V tile was published one iteration earlier).
+#ifndef RA_PIPE_PRE
+#define RA_PIPE_PRE 2
+#endif
+constexpr int kPre = RA_PIPE_PRE;
+template <int NP, int NS>
+constexpr bool is_pv(int k) {
+  if (k < kPre) return true;
+  const int r = k - kPre;  // alternate S, P-V while both are left
+  const int both = 2 * (NS < NP - kPre ? NS : NP - kPre);
+  if (r < both) return (r % 2) == 1;
+  return NS < NP - kPre;  // the longer kind finishes the iteration
 }
-
-// MFMA i of S^T = K Q^T for the tile in stage ST: key block kb = i % 2,
-// head_dim chunk c = i / 2.
-template <int D, int ST>
-__device__ __forceinline__ void s_mfma(int i, const uint32_t* k_addr, const bf16x8* qf, f32x16 (&sacc)[2]) {
-  using Ly = Layout<D>;
-  const int kb = i % 2;
-  const int c = i / 2;
-  const bf16x8 kf = *lds_ptr<bf16x8>(k_addr[c] + ST * Ly::kTileBytes + kb * 32 * Ly::kRowBytes);
-  sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sacc[kb], 0, 0, 0);
-}
-
-// LDS reads taken by MFMA k of the interleaved order P-V 0, S 0, P-V 1,
-// S 1, ..., then the P-V MFMAs past NS: two per P-V MFMA (none for the first
-// PRE, whose operands were read earlier), one per S MFMA.
-constexpr int pvs_reads(int k, int NP, int NS, int PRE) {
-  if (k >= NP + NS) return 0;
-  if (k < 2 * NS) return (k & 1) ? 1 : ((k / 2) < PRE ? 0 : 2);
-  return (NS + k - 2 * NS) < PRE ? 0 : 2;
-}
-constexpr int pvs_reads_before(int n, int NP, int NS, int PRE) {
-  int r = 0;
-  for (int k = 0; k < n; ++k) r += pvs_reads(k, NP, NS, PRE);
-  return r;
-}
-
-// Scheduling shape of NP P-V MFMAs interleaved with NS S MFMAs: the operands
-// of MFMA k + AHEAD are read right after MFMA k is issued.
-template <int NP, int NS, int PRE, int AHEAD>
-__device__ __forceinline__ void pipeline_pv_s() {
-  static_assert(NS <= NP, "more S than P-V MFMAs");
-  constexpr int kPro = pvs_reads_before(AHEAD, NP, NS, PRE);
-  if constexpr (kPro > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kPro, 0);
-#pragma unroll
-  for (int k = 0; k < NP + NS; ++k) {
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    const int r = pvs_reads(k + AHEAD, NP, NS, PRE);
-    if (r == 1) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    if (r == 2) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-  }
+template <int NP, int NS>
+constexpr int kind_index(int k) {
+  int n = 0;
+  for (int j = 0; j < k; ++j)
+    if (is_pv<NP, NS>(j) == is_pv<NP, NS>(k)) ++n;
+  return n;
 }
 
 template <int D>
 __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t n_items, int32_t items_per_xcd,
                                                              int32_t q_tiles) {
   using Ly = Layout<D>;
+  constexpr int NP = 4 * Ly::kDBlocks;  // P-V products per tile
+  constexpr int NS = 2 * Ly::kDChunks;  // S products per tile
   __shared__ __attribute__((aligned(1024))) char smem[Ly::kSmemBytes];
 
   // ---- work item ------------------------------------------------------------
@@ -199,7 +188,6 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
   const int lane = tid & 63;
   const int qcol = lane & 31;
   const int hh = lane >> 5;
-  const int group = wave >> 2;  // 0: first phase group, 1: one phase behind
 
   const int64_t row0 = (int64_t)tile * kBM;
   const int64_t r1 = (row0 + kBM < a.q_len) ? row0 + kBM : a.q_len;
@@ -223,17 +211,22 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
   };
 
   const uint32_t smem_base = lds_address(smem);
-  // Tile copies are issued by the waves that run a softmax phase, right after
-  // their softmax, where they would otherwise wait at the barrier; the matrix
-  // waves never stall on load issue. Group g copies half g of each tile.
-  auto issue = [&](int t) {
-    const uint32_t st = (uint32_t)(t % kStages) * Ly::kTileBytes;
-    issue_tile<D>(kg, vg, a.kv_len, tile_start(t), smem_base + st, smem_base + Ly::kVBase + st, group, wave & 3,
-                  lane);
+  TileCopier<D, false> kcopy;
+  TileCopier<D, true> vcopy;
+  kcopy.init(kg, wave, lane);
+  vcopy.init(vg, wave, lane);
+  auto issue_k = [&](int t) {
+    kcopy.copy(a.kv_len, tile_start(t), t < ntiles, smem_base + (uint32_t)(t % kStages) * Ly::kTileBytes, wave);
   };
-#pragma unroll
-  for (int t = 0; t < kPrefetch; ++t)
-    if (t < ntiles) issue(t);
+  auto issue_v = [&](int t) {
+    vcopy.copy(a.kv_len, tile_start(t), t < ntiles, smem_base + Ly::kVBase + (uint32_t)(t % kStages) * Ly::kTileBytes,
+               wave);
+  };
+  // K of tiles 0 and 1 first (the first products need them), and zeros into
+  // the V stage of "tile -1" (the stage of tile 3, requested in iteration 1)
+  issue_k(0);
+  issue_k(1);
+  vcopy.copy(a.kv_len, 0, false, smem_base + Ly::kVBase + 3u * Ly::kTileBytes, wave);
 
   // ---- Q^T fragments (B operand of S^T = K Q^T) ------------------------------
   bf16x8 qf[Ly::kDChunks];
@@ -275,10 +268,6 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
   const int32_t vend1 = row_visible_end(a, plan.r1, qpos);
   const float sl2 = a.scale_log2;
 
-  // Per-lane LDS addresses, fixed for the launch; every read below adds only a
-  // compile-time offset (stage, key block, slice) that fits the 16-bit
-  // offset field of the instruction.
-  // K read (A operand of S^T): row kb*32 + qcol, logical unit 2c + hh.
   uint32_t k_addr[Ly::kDChunks];
 #pragma unroll
   for (int c = 0; c < Ly::kDChunks; ++c) k_addr[c] = k_read_address<D>(smem_base, qcol, hh, c);
@@ -286,169 +275,259 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
 #pragma unroll
   for (int db = 0; db < Ly::kDBlocks; ++db) v_addr[db] = v_read_address<D>(smem_base, lane, db);
 
-  f32x16 sacc[2];
-  bf16x8 pf[2][2];
-  bf16x8 vpre[kVPre > 0 ? kVPre : 1];
+  f32x16 sacc[2][2];   // S^T of two tiles: [buffer][key block]
+  bf16x8 vpre[kPre];   // V^T operands of an iteration's first P-V products
+  bf16x8 pf[2][2][2];  // packed P^T of two tiles: [buffer][key block][16-key chunk]
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) sacc[kb][j] = 0.0f;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int c = 0; c < 2; ++c) pf[kb][c] = bf16x8{};
+    for (int c = 0; c < 2; ++c) pf[1][kb][c] = bf16x8{};  // the weights of "tile -1"
 
-  // Per wave the work is the sequence M_0 S_0 M_1 S_1 ... S_{n-1} M_n with
-  // M_v = (P V of tile v-1, S of tile v) on the matrix cores and S_t the
-  // softmax of tile t. Group 0 runs item i in phase i, group 1 in phase i+1.
-  // Only even phases start with a workgroup barrier (all waves pass n+1 of
-  // them); within the two phases between barriers each wave runs one matrix
-  // and one softmax phase at its own pace. The tile loop is unrolled by
-  // kStages so the stage is a compile-time constant.
-  int ph = 0;
-  // Tile t lands in stage t % kStages (four stages). Group 1 copies its half
-  // after its softmax of tile t-3 (phase 2t-4; its idle phase 0 for tile 2),
-  // group 0 after its softmax of tile t-2 (phase 2t-3); the stage last held
-  // tile t-4, read for the last time in phase 2t-5, so the barrier that
-  // opens phase 2t-4 lies between its last read and the copies. At the start of even
-  // phase 2u each wave waits until its copies of tile u have landed (its
-  // copies of tile u+1 were issued after them and may still be in flight;
-  // loads complete in order) and the barrier publishes tile u.
-  auto next_phase = [&]() {
-    const int u = ph >> 1;
-    if ((ph & 1) == 0) {
-      if (u < ntiles) {
-        if (kPrefetch == 2 && u + 1 < ntiles)
-          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kLoadsPerWave<D>) : "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
-      // Execution barrier only: a fence here would make every wave wait for
-      // all of its copies in flight, not just for the tile being published.
-      // Every LDS read of a matrix phase feeds an MFMA of that phase, so it
-      // has completed; reads issued at the end of a softmax phase (V^T
-      // operands of a tile published earlier) may still be in flight and are
-      // waited for at their first use.
-      asm volatile("s_barrier" ::: "memory");
-    }
-    // Odd phase boundaries need no barrier: nothing is published there, and
-    // every stage is refilled (after S_v: tile v+2 by group 0, tile v+3 by
-    // group 1) at least one even barrier after the last read of the tile it
-    // held.
-    ++ph;
-  };
-
-  // One loop iteration: M_v (P V of tile v-1 from stage ST_PREV, S of tile v
-  // from stage ST), then S_v.
-  auto iteration = [&](auto st_tag, int v) {
-    constexpr int ST = decltype(st_tag)::value;
-    constexpr int ST_PREV = (ST + kStages - 1) % kStages;
-    next_phase();
-    // ---- M_v: O^T += V^T P^T (tile v-1) interleaved with S^T = K Q^T (tile v).
-    // The two products use different accumulators, so alternating them keeps
-    // six independent MFMA chains in flight.
-    // v == 0 has no P-V yet (it is peeled off below); on the last iteration
-    // (v == ntiles) the S products read a stage holding an older tile and
-    // are never used, which keeps a single code path.
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) sacc[kb][j] = 0.0f;
-    if (v == 0) {
-#pragma unroll
-      for (int i = 0; i < 2 * Ly::kDChunks; ++i) s_mfma<D, ST>(i, k_addr, qf, sacc);
-      pipeline_lds_mfma<2 * Ly::kDChunks, 1, kLookahead>();
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4 * Ly::kDBlocks; ++i) {
-        if (i < kVPre)
-          pv_mfma<D>(i, vpre[i < kVPre ? i : 0], pf, oacc);
-        else
-          pv_mfma<D>(i, read_vt<D, ST_PREV>(i, v_addr), pf, oacc);
-        if (i < 2 * Ly::kDChunks) s_mfma<D, ST>(i, k_addr, qf, sacc);
-      }
-      pipeline_pv_s<4 * Ly::kDBlocks, 2 * Ly::kDChunks, kVPre, kPvsAhead>();
-    }
-    const bool do_s = v < ntiles;
-    if (do_s) {
-      next_phase();
-      // ---- softmax of tile v -------------------------------------------------------
-      const bool first_range = v < plan.r0.ntiles;
-      const int32_t start = tile_start(v);
-      if (start + kBN > (first_range ? plan.r0.full : plan.r1.full)) {
-        const int32_t lim = (first_range ? vend0 : vend1) - start;  // keys [0, lim) are visible
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int key = kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
-            if (key >= lim) sacc[kb][j] = -INFINITY;
-          }
-      }
-      float mx = sacc[0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kb][j]);
-      mx = max_with_partner(mx) * sl2;
-      const float cand = fmaxf(m_run, mx);
-      const bool need = cand > m_run + kRescaleThreshold;
-      if (__builtin_amdgcn_ballot_w64(need) != 0) {
-        const float m_upd = need ? cand : m_run;
-        const float alpha = (m_upd == m_run) ? 1.0f : exp2f(m_run - m_upd);
-#pragma unroll
-        for (int db = 0; db < Ly::kDBlocks; ++db)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
-        l_run *= alpha;
-        m_run = m_upd;
-      }
-      const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
-      float psum = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][j], sl2, -msub));
-          sacc[kb][j] = p;
-          psum += p;
-        }
-      l_run += psum;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) pf[kb][c] = pack_p(sacc[kb], 8 * c);
-      {
-        const int t = v + (group == 1 ? 3 : 2);
-        if (t >= kPrefetch && t < ntiles) issue(t);
-      }
-#pragma unroll
-      for (int i = 0; i < kVPre; ++i) vpre[i] = read_vt<D, ST>(i, v_addr);
-    }
-  };
-
-  // Everything loaded so far (Q, the incoming state, the first tiles) must
+  // Everything loaded so far (Q, the incoming state, K of tiles 0 and 1) must
   // be in registers / LDS before the loop. The builtin (not asm) form lets
   // the compiler see it, so it inserts no load waits inside the loop, where
   // the hardware counter also counts the tile copies in flight.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  // the copies iterations -2 and -1 would make (V of tile 0; K of 2, V of 1)
+  issue_v(0);
+  issue_k(2);
+  issue_v(1);
+  asm volatile("s_barrier" ::: "memory");  // K of tiles 0 and 1 visible to all waves
 
-  if (group == 1) {  // group 1 starts one phase late
-    next_phase();
-    if (kPrefetch < ntiles) issue(kPrefetch);
-  }
-  for (int v = 0; v <= ntiles; v += kStages) {
-    iteration(std::integral_constant<int, 0>{}, v);
-    if (v + 1 > ntiles) break;
-    iteration(std::integral_constant<int, 1>{}, v + 1);
-    if (v + 2 > ntiles) break;
-    iteration(std::integral_constant<int, 2>{}, v + 2);
-    if constexpr (kStages == 4) {
-      if (v + 3 > ntiles) break;
-      iteration(std::integral_constant<int, 3 % kStages>{}, v + 3);
+  // Tile t's softmax: mask (partial tiles only), then the speculative
+  // exponentials against the current reference. Returns the row maximum
+  // (in base-2 units, this lane's pair combined) and the lane's sum.
+  auto mask_tile = [&](f32x16 (&s)[2], int t) {
+    const bool first_range = t < plan.r0.ntiles;
+    const int32_t start = tile_start(t);
+    if (start + kBN > (first_range ? plan.r0.full : plan.r1.full)) {
+      // keys [0, lim) are visible; this lane holds keys 4*hh + (a constant)
+      const int32_t lim = (first_range ? vend0 : vend1) - start - 4 * hh;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int key = kb * 32 + 8 * (j >> 2) + (j & 3);
+          if (key >= lim) s[kb][j] = -INFINITY;
+        }
+    }
+  };
+
+  // Weights of a tile against reference msub, in place of its scores, packed
+  // into pb; returns this lane's sum of the fp32 weights.
+  auto weights = [&](f32x16 (&s)[2], float msub, bf16x8 (&pb)[2][2]) -> float {
+    float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        s[kb][j] = __builtin_amdgcn_exp2f(fmaf(s[kb][j], sl2, -msub));
+        part[j & 3] += s[kb][j];
+      }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) pb[kb][c] = pack_p(s[kb], 8 * c);
+    return (part[0] + part[1]) + (part[2] + part[3]);
+  };
+
+  // S^T of one tile from the K tile in stage ST into s.
+  auto scores = [&](auto st_tag, f32x16 (&s)[2]) {
+    constexpr int ST = decltype(st_tag)::value;
+    const f32x16 zero = {};
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int kb = i % 2;
+      const int c = i / 2;
+      const bf16x8 kf = *lds_ptr<bf16x8>(k_addr[c] + ST * Ly::kTileBytes + kb * 32 * Ly::kRowBytes);
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], c == 0 ? zero : s[kb], 0, 0, 0);
+    }
+  };
+
+  // The rare path after tile t's speculative weights (K of tile t still in
+  // stage ST): raise the reference to the tile's maximum where it passed it
+  // by more than the threshold, rescale O and l, and recompute the tile's
+  // scores and weights. O must already hold the products of tile t-1 (the
+  // compiler orders the rescale after them).
+  auto settle = [&](auto st_tag, f32x16 (&s)[2], int t, float mx, float& psum, bf16x8 (&pb)[2][2]) {
+    const float cand = fmaxf(m_run, mx);
+    const bool need = cand > m_run + kRescaleThreshold;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      const float m_upd = need ? cand : m_run;
+      const float alpha = (m_upd == m_run) ? 1.0f : exp2f(m_run - m_upd);
+#pragma unroll
+      for (int db = 0; db < Ly::kDBlocks; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
+      l_run *= alpha;
+      m_run = m_upd;
+      scores(st_tag, s);
+      mask_tile(s, t);
+      psum = weights(s, (m_run == -INFINITY) ? 0.0f : m_run, pb);
+    }
+    l_run += psum;
+  };
+
+  // End of iteration t: wait for this wave's copies of the tiles the next
+  // iteration reads (K of t+2, requested at the start of iteration t-1, and
+  // the older V of t), then publish them. Three copy groups issued since (V
+  // of t+1, K of t+3, V of t+2: a fixed number, empty tiles included) may
+  // stay in flight.
+  auto publish = [&]() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * kCopies<D>) : "memory");
+    asm volatile("s_barrier" ::: "memory");
+  };
+
+  // One iteration t with K of tile t+1 in stage SK and V of tile t-1 in
+  // stage SV; the softmax tile is sacc[BUF], the next S goes to
+  // sacc[BUF^1], the new weights to pf[BUF], the P-V products read
+  // pf[BUF^1]. Every iteration has the same shape: for t = 0 the weights of
+  // "tile -1" are zero and its V stage holds zeros, so those products add
+  // nothing; for the last tile the S products read a stage of zeros and are
+  // never used.
+  auto iteration = [&](auto sk_tag, auto sv_tag, auto buf_tag, int t) {
+    constexpr int SK = decltype(sk_tag)::value;
+    constexpr int SV = decltype(sv_tag)::value;
+    constexpr int BUF = decltype(buf_tag)::value;
+    constexpr int NM = NP + NS;      // products per iteration
+    constexpr int EPS = 32 / NM;     // softmax elements per slot
+    // K of tile t+3 goes to the stage of K of tile t-1 (last read before the
+    // previous barrier)
+    issue_k(t + kKAhead);
+    mask_tile(sacc[BUF], t);
+    const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
+    f32x16(&sc)[2] = sacc[BUF];
+    f32x16(&sn)[2] = sacc[BUF ^ 1];
+    const f32x16 zero = {};
+
+    // Slot k: product k, the operand read of product k + kAhead, and a fixed
+    // share of tile t's vector work: the exponentials of elements
+    // [k*EPS, (k+1)*EPS), the sums of the previous slot's elements (the
+    // exponential's latency), the maximum of two more elements while any
+    // are left, and one bf16 pair conversion two slots after both of its
+    // exponentials. Slots are fenced so the compiler keeps this interleave.
+    bf16x8 frag[NM];
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) frag[k] = vpre[k];
+    auto read_operand = [&](int k) {
+      const int i = kind_index<NP, NS>(k);
+      if (is_pv<NP, NS>(k)) {
+        frag[k] = read_vt<D, SV>(i, v_addr);
+      } else {
+        const int kb = i % 2;
+        const int c = i / 2;
+        frag[k] = *lds_ptr<bf16x8>(k_addr[c] + SK * Ly::kTileBytes + kb * 32 * Ly::kRowBytes);
+      }
+    };
+    float p[32];
+    float part[4];
+    float mx = sc[0][0];
+    bf16x2 pairs[16];
+    auto elem = [&](int e) -> float { return sc[e / 16][e % 16]; };
+#pragma unroll
+    for (int k = kPre; k < kAhead; ++k) read_operand(k);
+#pragma unroll
+    for (int k = 0; k < NM; ++k) {
+      const int i = kind_index<NP, NS>(k);
+      if (is_pv<NP, NS>(k)) {
+        const int db = i % Ly::kDBlocks;
+        const int kc = i / Ly::kDBlocks;
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[k], pf[BUF ^ 1][kc / 2][kc % 2], oacc[db], 0, 0, 0);
+      } else {
+        const int kb = i % 2;
+        const int c = i / 2;
+        sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[k], qf[c], c == 0 ? zero : sn[kb], 0, 0, 0);
+      }
+      if (k + kAhead < NM) read_operand(k + kAhead);
+#pragma unroll
+      for (int e = k * EPS; e < (k + 1) * EPS; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(elem(e), sl2, -msub));
+      if (k >= 1) {
+#pragma unroll
+        for (int e = (k - 1) * EPS; e < k * EPS; ++e) part[e & 3] = e < 4 ? p[e] : part[e & 3] + p[e];
+      }
+      if (k < 16) mx = fmaxf(fmaxf(mx, elem(2 * k)), elem(2 * k + 1));
+#pragma unroll
+      for (int m = 0; m < 16; ++m)
+        if ((2 * m + 1) / EPS + 2 == k) pairs[m] = __builtin_convertvector((f32x2){p[2 * m], p[2 * m + 1]}, bf16x2);
+      if (k == NM / 2) issue_v(t + kVAhead);  // V of tile t+2 (its stage held V of tile t-2)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int e = (NM - 1) * EPS; e < 32; ++e) part[e & 3] = e < 4 ? p[e] : part[e & 3] + p[e];
+#pragma unroll
+    for (int m = 0; m < 16; ++m)
+      if ((2 * m + 1) / EPS + 2 >= NM) pairs[m] = __builtin_convertvector((f32x2){p[2 * m], p[2 * m + 1]}, bf16x2);
+    if (NM < 16) {
+#pragma unroll
+      for (int k = NM; k < 16; ++k) mx = fmaxf(fmaxf(mx, elem(2 * k)), elem(2 * k + 1));
+    }
+    // pairs m = 8 kb + 4 c + q hold keys 8 c + 2 q, +1 of key block kb
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int m0 = 8 * kb + 4 * c;
+        const auto ab = __builtin_shufflevector(pairs[m0], pairs[m0 + 1], 0, 1, 2, 3);
+        const auto cd = __builtin_shufflevector(pairs[m0 + 2], pairs[m0 + 3], 0, 1, 2, 3);
+        pf[BUF][kb][c] = __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    float psum = (part[0] + part[1]) + (part[2] + part[3]);
+    mx = max_with_partner(mx) * sl2;
+    // The rare path below overwrites the speculative weights; without these
+    // uses the compiler would sink their computation past the branch, out of
+    // the interleaved slots.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) asm volatile("" ::"v"(__builtin_bit_cast(i32x4, pf[BUF][kb][c])));
+    asm volatile("" ::"v"(psum));
+    settle(std::integral_constant<int, (SK + 3) % 4>{}, sacc[BUF], t, mx, psum, pf[BUF]);
+    // operands of the next iteration's first P-V products: V of tile t, in
+    // stage (SV + 1) % 4, published at the end of the previous iteration
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) vpre[k] = read_vt<D, (SV + 1) % 4>(k, v_addr);
+    publish();
+  };
+
+  // The P-V products of the last tile (V in stage SV, weights in pf[BUF]).
+  auto last_pv = [&](auto sv_tag, auto buf_tag) {
+    constexpr int SV = decltype(sv_tag)::value;
+    constexpr int BUF = decltype(buf_tag)::value;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int db = i % Ly::kDBlocks;
+      const int kc = i / Ly::kDBlocks;
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_vt<D, SV>(i, v_addr), pf[BUF][kc / 2][kc % 2], oacc[db],
+                                                         0, 0, 0);
+    }
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+
+  if (ntiles > 0) {
+    scores(I0{}, sacc[0]);  // S of tile 0 (stage 0)
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) vpre[k] = read_vt<D, 3>(k, v_addr);  // "tile -1": zeros
+    // iteration t: K of t+1 in stage (t+1)%4, V of t-1 in (t-1)%4, buffer t%2
+    for (int t = 0; t < ntiles; t += 4) {
+      iteration(I1{}, I3{}, I0{}, t);
+      if (t + 1 >= ntiles) break;
+      iteration(I2{}, I0{}, I1{}, t + 1);
+      if (t + 2 >= ntiles) break;
+      iteration(I3{}, I1{}, I0{}, t + 2);
+      if (t + 3 >= ntiles) break;
+      iteration(I0{}, I2{}, I1{}, t + 3);
+    }
+    switch ((ntiles - 1) & 3) {  // P-V of the last tile
+      case 0: last_pv(I0{}, I0{}); break;
+      case 1: last_pv(I1{}, I1{}); break;
+      case 2: last_pv(I2{}, I0{}); break;
+      default: last_pv(I3{}, I1{}); break;
     }
   }
-  if (group == 0) next_phase();  // group 0 ends one phase early
 
   // ---- write back ---------------------------------------------------------------
   const float l_tot = sum_with_partner(l_run);
