@@ -97,16 +97,18 @@ __device__ __forceinline__ bf16x8 read_tr(const uint32_t (&lo)[N], const uint32_
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Copy `nb` 1 KB blocks of a 64-row tile (rows [0, nrows) of `src` valid,
-// the rest read as zero) into LDS at dst, blocks first_block .. +nb.
-template <int D>
-__device__ __forceinline__ void copy_tile_blocks(const i32x4& rsrc, uint32_t dst, int first_block, int nb, int lane) {
-  for (int i = 0; i < nb; ++i) {
-    const int blk = first_block + i;
-    const int u = blk * 64 + lane;
+// This lane's byte offsets for a wave's NB consecutive 1 KB blocks of a
+// 64-row tile, first block `first_block`, in the form dma16_blocks takes
+// (block j's offset minus 1024 j); the lane fills stored unit p of row r and
+// fetches logical unit p ^ swz(r).
+template <int D, int NB>
+__device__ __forceinline__ void tile_block_offsets(int first_block, int lane, int (&voff)[NB]) {
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int u = (first_block + i) * 64 + lane;
     const int r = u / BL<D>::kUnits;
     const int p = u % BL<D>::kUnits;
-    dma16(rsrc, dst + blk * 1024, r * BL<D>::kRowB + ((p ^ BL<D>::swz(r)) << 4));
+    voff[i] = r * BL<D>::kRowB + ((p ^ BL<D>::swz(r)) << 4) - i * 1024;
   }
 }
 
@@ -199,15 +201,19 @@ __global__ void __launch_bounds__(kQWaves * 64) bwd_dq_kernel(BwdArgs a, int32_t
     return t < plan.r0.ntiles ? plan.r0.begin + t * 64 : plan.r1.begin + (t - plan.r0.ntiles) * 64;
   };
   const uint32_t smem_base = lds_address(smem);
+  // K and V tiles share the swizzle, so one set of per-lane offsets serves both
+  constexpr int kNB = kQCopies / 2;
+  int voff[kNB];
+  tile_block_offsets<D, kNB>(wave * kNB, lane, voff);
+  const uint64_t kbase = uniform_address(kg), vbase = uniform_address(vg);
   auto issue = [&](int t) {
     const int32_t start = tile_start(t);
-    const int64_t left = s.kv_len - start;
-    const int nbytes = (int)((left < 64 ? left : 64) * kRowB);
-    const uint32_t dst = smem_base + (uint32_t)(t % kQStages) * kQStageB;
-    const i32x4 rk = buffer_resource(kg + (int64_t)start * kRowB, nbytes);
-    const i32x4 rv = buffer_resource(vg + (int64_t)start * kRowB, nbytes);
-    copy_tile_blocks<D>(rk, dst, wave * (kQCopies / 2), kQCopies / 2, lane);
-    copy_tile_blocks<D>(rv, dst + kTileB, wave * (kQCopies / 2), kQCopies / 2, lane);
+    const int32_t left = (int32_t)s.kv_len - start;  // row counts are < 2^31
+    const int nbytes = (left < 64 ? left : 64) * kRowB;
+    const uint32_t dst = smem_base + (uint32_t)(t % kQStages) * kQStageB + (uint32_t)(wave * kNB * 1024);
+    const uint64_t off = (uint64_t)start * kRowB;
+    dma16_blocks<kNB>(resource_at(kbase, off, nbytes), dst, voff);
+    dma16_blocks<kNB>(resource_at(vbase, off, nbytes), dst + kTileB, voff);
   };
   if (ntiles > 0) issue(0);
   if (ntiles > 1) issue(1);
@@ -486,6 +492,12 @@ bwd_dkdv_kernel(BwdArgs a, int32_t k_tiles) {
     *r = tt < ra0.ntiles ? &ra0 : &ra1;
     *rs = (*r)->begin + (int64_t)(tt < ra0.ntiles ? tt : tt - ra0.ntiles) * 64;
   };
+  // Q and dO tiles share the swizzle, so one set of per-lane offsets serves both
+  int voff[kKCopies];
+  tile_block_offsets<D, kKCopies>(wave * kKCopies, lane, voff);
+  const int toff[1] = {lane * 16};  // a block of 64 row terms
+  const uint64_t qbase = uniform_address(s.q), obase = uniform_address(a.dout);
+  const uint64_t tbase = uniform_address(a.terms);
   auto issue = [&](int it) {
     int32_t h;
     const RowRange* r;
@@ -495,12 +507,13 @@ bwd_dkdv_kernel(BwdArgs a, int32_t k_tiles) {
     const int nrows = (int)(left < 64 ? left : 64);
     const int64_t first = ((int64_t)b * s.heads_q + h) * s.q_len + rs;
     const uint32_t dst = smem_base + (uint32_t)(it % kKStages) * kKStageB;
-    const i32x4 rq = buffer_resource(static_cast<const unsigned short*>(s.q) + first * kD, nrows * kRowB);
-    const i32x4 ro = buffer_resource(static_cast<const unsigned short*>(a.dout) + first * kD, nrows * kRowB);
-    copy_tile_blocks<D>(rq, dst, wave * kKCopies, kKCopies, lane);
-    copy_tile_blocks<D>(ro, dst + kKOffDo, wave * kKCopies, kKCopies, lane);
-    if (wave == 0) dma16(buffer_resource(a.terms + first, nrows * 4), dst + kKOffC, lane * 16);
-    if (wave == 1) dma16(buffer_resource(a.terms + n_rows + first, nrows * 4), dst + kKOffE, lane * 16);
+    const uint32_t wdst = dst + (uint32_t)(wave * kKCopies * 1024);
+    const uint64_t off = (uint64_t)first * kRowB;
+    dma16_blocks<kKCopies>(resource_at(qbase, off, nrows * kRowB), wdst, voff);
+    dma16_blocks<kKCopies>(resource_at(obase, off, nrows * kRowB), wdst + kKOffDo, voff);
+    if (wave == 0) dma16_blocks<1>(resource_at(tbase, (uint64_t)first * 4, nrows * 4), dst + kKOffC, toff);
+    if (wave == 1)
+      dma16_blocks<1>(resource_at(tbase, (uint64_t)(n_rows + first) * 4, nrows * 4), dst + kKOffE, toff);
   };
   issue(0);
   if (total > 1) issue(1);

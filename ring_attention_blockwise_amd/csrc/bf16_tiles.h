@@ -72,37 +72,63 @@ __device__ __forceinline__ bf16x8 pack_p(const f32x16& s, int base) {
   return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Raw buffer resource over `nbytes` bytes at `base` (wave-uniform).
-__device__ __forceinline__ i32x4 buffer_resource(const void* base, int nbytes) {
-  const uint64_t p = reinterpret_cast<uint64_t>(base);
-  i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
-  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));  // stride 0
-  r[2] = __builtin_amdgcn_readfirstlane(nbytes);
-  r[3] = kBufferWord3;
-  return r;
-}
-
 template <class T>
 __device__ __forceinline__ const __attribute__((address_space(3))) T* lds_ptr(uint32_t addr) {
   return (const __attribute__((address_space(3))) T*)(uintptr_t)addr;
 }
 
-// One 16-byte-per-lane buffer load straight into LDS: lane i's 16 bytes land
-// at LDS byte address lds_base + 16*i. Issued through asm so the compiler
-// does not order later LDS reads of *other* stages behind it; the kernel
-// waits for it explicitly (vmcnt) before the barrier that publishes a tile.
-// M0 (the LDS destination) is saved and restored around the load.
-__device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t lds_base, int voff) {
-  int saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds_base), "v"(voff), "s"(rsrc)
-      : "memory");
+// A wave-uniform 64-bit address held in SGPRs.
+__device__ __forceinline__ uint64_t uniform_address(const void* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Raw buffer resource over `nbytes` bytes at the uniform address base + off.
+__device__ __forceinline__ i32x4 resource_at(uint64_t base, uint64_t off, int nbytes) {
+  const uint64_t a = base + off;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));  // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane(nbytes);
+  r[3] = kBufferWord3;
+  return r;
+}
+
+// A wave's NB consecutive 1 KB blocks of a tile copied into LDS with one M0
+// write: lane i of block j lands at lds_dst + 1024 j + 16 i. The per-lane
+// byte offsets are computed once (block j's minus 1024 j: the instruction
+// offset 1024 j moves the global and the LDS address alike). M0 is declared
+// clobbered; nothing else in these kernels keeps a value in it.
+template <int NB>
+__device__ __forceinline__ void dma16_blocks(const i32x4& rsrc, uint32_t lds_dst, const int (&voff)[NB]) {
+  static_assert(NB == 1 || NB == 2 || NB == 4, "one, two or four blocks");
+  if constexpr (NB == 4)
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+        "buffer_load_dwordx4 %3, %2, 0 offen offset:1024 lds\n\t"
+        "buffer_load_dwordx4 %4, %2, 0 offen offset:2048 lds\n\t"
+        "buffer_load_dwordx4 %5, %2, 0 offen offset:3072 lds"
+        :
+        : "s"(lds_dst), "v"(voff[0]), "s"(rsrc), "v"(voff[1 % NB]), "v"(voff[2 % NB]), "v"(voff[3 % NB])
+        : "memory", "m0");
+  else if constexpr (NB == 2)
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+        "buffer_load_dwordx4 %3, %2, 0 offen offset:1024 lds"
+        :
+        : "s"(lds_dst), "v"(voff[0]), "s"(rsrc), "v"(voff[1 % NB])
+        : "memory", "m0");
+  else
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        :
+        : "s"(lds_dst), "v"(voff[0]), "s"(rsrc)
+        : "memory", "m0");
 }
 
 __device__ __forceinline__ uint32_t lds_address(const void* p) {

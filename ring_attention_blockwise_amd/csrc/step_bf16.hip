@@ -59,24 +59,19 @@ constexpr int kCopies = Layout<D>::kTileBytes / 1024 / kWaves;
 
 // Copies of one tensor (K or V) of one head into the LDS rings. Set up once
 // per work item: the head's base address in SGPRs and this lane's byte
-// offsets for the wave's kCopies 1 KB blocks of a tile (block i > 0 is
-// reached through the instruction offset i * 1024, which moves the global and
-// the LDS address alike, so one M0 value serves all of them).
+// offsets for the wave's kCopies 1 KB blocks of a tile (dma16_blocks).
 template <int D, bool IS_V>
 struct TileCopier {
   using Ly = Layout<D>;
-  uint32_t base_lo, base_hi;
+  uint64_t base;
   int voff[kCopies<D>];
 
   __device__ __forceinline__ void init(const char* g, int wave, int lane) {
-    const uint64_t p = reinterpret_cast<uint64_t>(g);
-    base_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
-    base_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
+    base = uniform_address(g);
 #pragma unroll
     for (int i = 0; i < kCopies<D>; ++i) {
       // lane fills stored unit q of row r and fetches logical unit q ^ swz(r)
-      const int b = wave * kCopies<D> + i;  // 1 KB block of the tile
-      const int u = b * 64 + lane;
+      const int u = (wave * kCopies<D> + i) * 64 + lane;
       const int r = u / Ly::kUnits;
       const int q = u % Ly::kUnits;
       const int swz = IS_V ? Ly::v_swz(r) : Ly::k_swz(r);
@@ -93,31 +88,8 @@ struct TileCopier {
   __device__ __forceinline__ void copy(int64_t kv_len, int32_t start, bool exists, uint32_t stage, int wave) const {
     const int32_t left = exists ? (int32_t)kv_len - start : 0;  // row counts are < 2^31
     const int nbytes = (left < kBN ? left : kBN) * Ly::kRowBytes;
-    const uint64_t base = (((uint64_t)base_hi << 32) | base_lo) + (exists ? (uint64_t)start * Ly::kRowBytes : 0);
-    i32x4 rs;
-    rs[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)base);
-    rs[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32));  // stride 0
-    rs[2] = __builtin_amdgcn_readfirstlane(nbytes);
-    rs[3] = kBufferWord3;
-    const uint32_t m0 = stage + (uint32_t)(wave * kCopies<D> * 1024);
-    static_assert(kCopies<D> == 1 || kCopies<D> == 2, "one or two 1 KB blocks per wave");
-    // M0 holds the LDS destination of the copies; it is declared clobbered
-    // (nothing else in these kernels keeps a value in it).
-    if constexpr (kCopies<D> == 2)
-      asm volatile(
-          "s_mov_b32 m0, %0\n\t"
-          "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
-          "buffer_load_dwordx4 %3, %2, 0 offen offset:1024 lds"
-          :
-          : "s"(m0), "v"(voff[0]), "s"(rs), "v"(voff[kCopies<D> - 1])
-          : "memory", "m0");
-    else
-      asm volatile(
-          "s_mov_b32 m0, %0\n\t"
-          "buffer_load_dwordx4 %1, %2, 0 offen lds"
-          :
-          : "s"(m0), "v"(voff[0]), "s"(rs)
-          : "memory", "m0");
+    const uint64_t off = exists ? (uint64_t)start * Ly::kRowBytes : 0;
+    dma16_blocks<kCopies<D>>(resource_at(base, off, nbytes), stage + (uint32_t)(wave * kCopies<D> * 1024), voff);
   }
 };
 
