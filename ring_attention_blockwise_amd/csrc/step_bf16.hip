@@ -25,11 +25,13 @@
 //  * K and V tiles are copied HBM -> LDS by 16-byte buffer-to-LDS loads into
 //    two rings of four stages each: K of tile t+3 at the start of iteration
 //    t, V of tile t+2 in its middle (every wave copies one eighth of each),
-//    so a copy has about two iterations to land. One workgroup barrier per
-//    iteration publishes K of tile t+2 and V of tile t. Each copy goes to a
-//    stage whose last reader ran before the previous barrier (K of tile t is
-//    read by the products of iteration t-1 and by the rare path of iteration
-//    t).
+//    so a copy has one and a half to two iterations to land. One workgroup
+//    barrier per iteration, at the end of iteration t, publishes K of tile
+//    t+2 and V of tile t+1 (V of tile t+1 is first read at the end of
+//    iteration t+1, for the first P-V products of the next iteration). Each
+//    copy goes to a stage whose last reader ran before the previous barrier
+//    (K of tile t is read by the products of iteration t-1 and by the rare
+//    path of iteration t).
 //  * LDS layout, swizzle, operand lane layouts and the transposed V reads are
 //    those of bf16_tiles.h.
 #include <type_traits>
@@ -194,10 +196,12 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
     vcopy.copy(a.kv_len, tile_start(t), t < ntiles, smem_base + Ly::kVBase + (uint32_t)(t % kStages) * Ly::kTileBytes,
                wave);
   };
-  // K of tiles 0 and 1 first (the first products need them), and zeros into
-  // the V stage of "tile -1" (the stage of tile 3, requested in iteration 1)
+  // K of tiles 0 and 1 and V of tile 0 first (iteration 0 reads them), and
+  // zeros into the V stage of "tile -1" (the stage of tile 3, requested in
+  // iteration 1)
   issue_k(0);
   issue_k(1);
+  issue_v(0);
   vcopy.copy(a.kv_len, 0, false, smem_base + Ly::kVBase + 3u * Ly::kTileBytes, wave);
 
   // ---- Q^T fragments (B operand of S^T = K Q^T) ------------------------------
@@ -260,11 +264,10 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
   // the compiler see it, so it inserts no load waits inside the loop, where
   // the hardware counter also counts the tile copies in flight.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  // the copies iterations -2 and -1 would make (V of tile 0; K of 2, V of 1)
-  issue_v(0);
+  // the copies iteration -1 would make (K of 2, V of 1)
   issue_k(2);
   issue_v(1);
-  asm volatile("s_barrier" ::: "memory");  // K of tiles 0 and 1 visible to all waves
+  asm volatile("s_barrier" ::: "memory");  // K of tiles 0 and 1, V of 0 visible to all waves
 
   // Tile t's softmax: mask (partial tiles only), then the speculative
   // exponentials against the current reference. Returns the row maximum
@@ -340,13 +343,14 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
     l_run += psum;
   };
 
-  // End of iteration t: wait for this wave's copies of the tiles the next
-  // iteration reads (K of t+2, requested at the start of iteration t-1, and
-  // the older V of t), then publish them. Three copy groups issued since (V
-  // of t+1, K of t+3, V of t+2: a fixed number, empty tiles included) may
-  // stay in flight.
+  // End of iteration t: wait for this wave's copies of the tiles that
+  // iteration t+1 reads, then publish them: K of t+2 (its S products,
+  // requested at the start of iteration t-1) and V of t+1 (read at the end
+  // of iteration t+1 for the first P-V products of iteration t+2, requested
+  // in the middle of iteration t-1). The two copy groups issued since (K of
+  // t+3, V of t+2: a fixed number, empty tiles included) may stay in flight.
   auto publish = [&]() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * kCopies<D>) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kCopies<D>) : "memory");
     asm volatile("s_barrier" ::: "memory");
   };
 
@@ -456,6 +460,7 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
     settle(std::integral_constant<int, (SK + 3) % 4>{}, sacc[BUF], t, mx, psum, pf[BUF]);
     // operands of the next iteration's first P-V products: V of tile t, in
     // stage (SV + 1) % 4, published at the end of the previous iteration
+    // (for t = 0, by the barrier before the loop)
 #pragma unroll
     for (int k = 0; k < kPre; ++k) vpre[k] = read_vt<D, (SV + 1) % 4>(k, v_addr);
     publish();
