@@ -4,9 +4,10 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A bench "step" is one whole ring_attn_forward: every ring step of the
-device's share (the double-buffered receive of the next K/V block on a side
-stream, the causal-tiled step kernels) and the fused finalize, over seeded
-synthetic Q/K/V already resident in HBM. Prints ONE JSON line.
+device's share (the causal-tiled step kernels, each also receiving the next
+K/V block into the free slot, unless --receive memcpy) and the fused
+finalize, over seeded synthetic Q/K/V already resident in HBM. Prints ONE
+JSON line.
 
 value     effective causal attention TFLOP/s of the whole forward:
           sum over steps of 4 * head_dim * heads_q * batch * (visible pairs),
@@ -219,6 +220,52 @@ def traffic_from_profile(kernel_name, workload_name, sources=KERNEL_SOURCES):
     return rec.get("bytes_per_launch")
 
 
+def receive_modes(share, ws, out, lse, K, copy_stream, timed_ms, timed_mode, rounds=5):
+    """The forward with each receive copy, and the same step kernels with no
+    receive at all (ring_attn_step over the blocks in place, no finalize:
+    the fused finalize of the last step writes less than a plain step, so
+    this baseline is, if anything, slightly slow). The modes are timed in
+    turn, `rounds` times over, and each reports its median (ms per forward),
+    so that clock drift over the run does not favour one of them; overhead
+    = forward / no-receive - 1."""
+    import torch
+    from ring_attention_blockwise_amd import harness
+    cur = torch.cuda.current_stream()
+    wl = share.workload
+    n = max(2, K // 2)
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(cur)
+        for _ in range(n):
+            fn()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    state = harness.new_state(share)
+
+    def fwd(mode, cs):
+        return lambda: harness.run_forward(share, copy_stream=cs, workspace=ws, out=out, lse=lse, receive=mode)
+
+    modes = {"no_receive": lambda: harness.run_steps(share, range(wl.world), state=state),
+             "fused": fwd("fused", None), "memcpy_side_stream": fwd("memcpy", copy_stream),
+             "memcpy_compute_stream": fwd("memcpy", None)}
+    for fn in modes.values():
+        fn()
+    torch.cuda.synchronize()
+    runs = {k: [] for k in modes}
+    for _ in range(rounds):
+        for k, fn in modes.items():
+            runs[k].append(timed(fn))
+    ms = {k: float(np.median(v)) for k, v in runs.items()}
+    base = ms["no_receive"]
+    return {"timed_forwards": timed_mode, "rounds": rounds, "forwards_per_round": n,
+            "ms": {k: round(v, 4) for k, v in ms.items()},
+            "overhead_vs_no_receive": {k: round(v / base - 1.0, 4) for k, v in ms.items() if k != "no_receive"},
+            "timed_forward_overhead": round(timed_ms / base - 1.0, 4)}
+
+
 def hbm_kernels(share, reps=20):
     """GB/s of the HBM-bound pieces of the path at the share's shapes: the
     state merge, the finalize pass and the D2D receive copy of one K block
@@ -405,6 +452,10 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--rank", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--receive", default="auto", choices=["auto", "memcpy", "fused"],
+                    help="receive copy of the timed forwards (memcpy: hipMemcpyAsync on a side stream)")
+    ap.add_argument("--forwards-only", action="store_true",
+                    help="time the forwards and skip every other measurement (for kernel traces)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass of the workload's share instead of the forward")
     args = ap.parse_args()
@@ -451,8 +502,9 @@ def main():
     K, Wm = args.steps, args.warmup
     events = [ra.StepEvents(2 * wl.world) for _ in range(K)]
 
+    recv = args.receive
     for _ in range(Wm):
-        harness.run_forward(share, copy_stream=copy_stream, workspace=ws, out=out, lse=lse)
+        harness.run_forward(share, copy_stream=copy_stream, workspace=ws, out=out, lse=lse, receive=recv)
     torch.cuda.synchronize()
     log(f"warmup done ({Wm} forwards)")
 
@@ -462,7 +514,7 @@ def main():
     wall0 = time.perf_counter()
     for i in range(K):
         harness.run_forward(share, copy_stream=copy_stream, workspace=ws, out=out, lse=lse,
-                            step_events=events[i])
+                            step_events=events[i], receive=recv)
     stop.record(cur)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -487,11 +539,36 @@ def main():
     traffic = traffic_from_profile(kernel_name, wl.name)
     value = total_flops / (ms_per_step * 1e-3) / 1e12
 
+    if args.forwards_only:
+        graph_ms = receive = hbm = probe = balance = cpu = None
+        args.no_cpu_baseline = True
+    else:
+        graph_ms, receive, hbm, probe, balance = extras(share, ws, out, lse, K, copy_stream, ms_per_step, recv, wl)
+    cpu = None
+    if not args.no_cpu_baseline:
+        if wl.local_len * wl.heads_q * wl.batch * wl.total_len <= SMALL_SHARE_PAIRS:
+            log("timing the CPU oracle on the whole share (all threads, then one)")
+            cpu = cpu_baseline_full(wl, rank)
+        else:
+            log("timing the CPU oracle on a bounded sample")
+            cpu = cpu_baseline(wl, rank, total_flops)
+    rec = record(args, wl, rank, K, Wm, value, ms_per_step, bf16, total_flops, launched, avg_launch_ms, per_step_ms,
+                 achieved, peak, traffic, receive, graph_ms, hbm, probe, balance, cpu)
+    print(json.dumps(rec), flush=True)
+    for ev in events:
+        ev.close()
+
+
+def extras(share, ws, out, lse, K, copy_stream, ms_per_step, recv, wl):
+    """Graph replay, receive modes, HBM-bound kernels, matrix-core probe, load balance."""
+    import torch
+    from ring_attention_blockwise_amd import harness
+    cur = torch.cuda.current_stream()
     # The same forward captured once into a HIP graph and replayed: identical
     # work (every step kernel and receive copy), without per-launch host cost.
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        harness.run_forward(share, copy_stream=copy_stream, workspace=ws, out=out, lse=lse)
+        harness.run_forward(share, copy_stream=copy_stream, workspace=ws, out=out, lse=lse, receive=recv)
     torch.cuda.synchronize()
     graph.replay()
     torch.cuda.synchronize()
@@ -505,22 +582,20 @@ def main():
     del graph
     log(f"graph replay: {graph_ms:.3f} ms per forward")
 
+    receive = receive_modes(share, ws, out, lse, K, copy_stream, ms_per_step, recv)
+    log(f"receive: {receive}")
+
     hbm = hbm_kernels(share)
     log(f"HBM-bound pieces: {hbm}")
 
     probe = mfma_probe()
     log(f"matrix-core probe: {probe}")
     balance = load_balance(wl)
+    return graph_ms, receive, hbm, probe, balance
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        if wl.local_len * wl.heads_q * wl.batch * wl.total_len <= SMALL_SHARE_PAIRS:
-            log("timing the CPU oracle on the whole share (all threads, then one)")
-            cpu = cpu_baseline_full(wl, rank)
-        else:
-            log("timing the CPU oracle on a bounded sample")
-            cpu = cpu_baseline(wl, rank, total_flops)
 
+def record(args, wl, rank, K, Wm, value, ms_per_step, bf16, total_flops, launched, avg_launch_ms, per_step_ms,
+           achieved, peak, traffic, receive, graph_ms, hbm, probe, balance, cpu):
     rec = {
         "metric": "effective causal attention TFLOP/s per ring step at 1 GPU; % of bf16 MFMA peak",
         "value": round(value, 3),
@@ -539,6 +614,7 @@ def main():
             "heads_kv": wl.heads_kv, "head_dim": wl.head_dim, "local_len": wl.local_len,
             "global_seq_len": wl.total_len, "world": wl.world, "rank": rank, "partition": wl.partition,
             "ring_steps": wl.world, "parallelism": "one device's share of a simulated ring",
+            "receive": args.receive,
         },
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "effective_tflop_per_forward": round(total_flops / 1e12, 4),
@@ -556,16 +632,16 @@ def main():
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
         },
-        "graph_forward": {"ms_per_forward": round(graph_ms, 4),
-                          "value": round(total_flops / (graph_ms * 1e-3) / 1e12, 3)},
+        "receive": receive,
+        "graph_forward": None if graph_ms is None else {
+            "ms_per_forward": round(graph_ms, 4), "value": round(total_flops / (graph_ms * 1e-3) / 1e12, 3)},
         "hbm_kernels": hbm,
-        "mfma_probe": dict(probe, step_kernel_frac_of_probe=round(achieved / probe["tflops"], 4) if bf16 else None),
+        "mfma_probe": None if probe is None else dict(
+            probe, step_kernel_frac_of_probe=round(achieved / probe["tflops"], 4) if bf16 else None),
         "load_balance": balance,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(rec), flush=True)
-    for ev in events:
-        ev.close()
+    return rec
 
 
 if __name__ == "__main__":

@@ -146,7 +146,26 @@ typedef struct {
   int32_t reverse_order;          /* 0: step s uses block (rank - s) mod n (blocks
                                      are sent to rank + 1, as [HC]'s code does);
                                      1: block (rank + s) mod n ([HC]'s 6.1 text) */
+  int32_t receive;                /* RA_RECV_*: how a block is copied into its
+                                     receive slot (the result is the same) */
 } ra_ring_desc;
+
+/* Receive copy of the ring drivers (desc->receive).
+ * RA_RECV_MEMCPY: hipMemcpyAsync of the K and V block on copy_stream (or on
+ *   compute_stream when copy_stream is NULL).
+ * RA_RECV_FUSED: the bf16 step kernel of step s copies the block of step
+ *   s + 1 into its slot while it computes: the work items of the launch
+ *   each move a share of it through a small LDS staging ring, one 1 KB
+ *   piece per wave per key tile, so the copy runs on the compute units the
+ *   step already holds (a separate copy kernel only gets compute units
+ *   between step workgroups). A step that launches no kernel (no visible
+ *   key) or computes in fp32 falls back to hipMemcpyAsync on
+ *   compute_stream. copy_stream is not used. Same results bit for bit.
+ * RA_RECV_AUTO: RA_RECV_FUSED for bf16, RA_RECV_MEMCPY for fp32.
+ * ring_attn_backward always copies with hipMemcpyAsync. */
+#define RA_RECV_AUTO   0
+#define RA_RECV_MEMCPY 1
+#define RA_RECV_FUSED  2
 
 /* Bytes of workspace ring_attn_forward needs: two receive slots for one K/V
  * block each, the fp32 state and alignment padding. Returns 0 on a bad desc. */
@@ -158,9 +177,9 @@ size_t ring_attn_forward_workspace_size(const ra_ring_desc* desc);
  *   v_blocks[j]    HOST arrays of `world` DEVICE pointers: the K/V block device j
  *                  holds, [B, Hkv, c, d], rows in device j's partition order.
  *                  Block rank is used in place; every other block is first
- *                  copied into a receive slot of the workspace by
- *                  hipMemcpyAsync on copy_stream while the previous step
- *                  computes on compute_stream (the simulated receive; events
+ *                  copied into a receive slot of the workspace on copy_stream
+ *                  while the previous step computes on compute_stream (the
+ *                  simulated receive; desc->receive picks the copy; events
  *                  order the two streams, two slots alternate).
  *   out, lse       as ring_attn_finalize.
  *   compute_stream, copy_stream  hipStream_t (distinct; copy_stream may be NULL

@@ -22,6 +22,8 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
 CONTIGUOUS, ZIGZAG, STRIPED = 0, 1, 2
 PARTITIONS = {"contiguous": CONTIGUOUS, "zigzag": ZIGZAG, "striped": STRIPED}
+RECV_AUTO, RECV_MEMCPY, RECV_FUSED = 0, 1, 2
+RECEIVES = {"auto": RECV_AUTO, "memcpy": RECV_MEMCPY, "fused": RECV_FUSED}
 STEP_INIT = 1
 BWD_INIT_DQ = 1
 
@@ -57,6 +59,7 @@ class RingDesc(ctypes.Structure):
         ("head_dim", ctypes.c_int32), ("local_len", ctypes.c_int64), ("dtype", ctypes.c_int32),
         ("causal", ctypes.c_int32), ("scale", ctypes.c_float), ("world", ctypes.c_int32),
         ("rank", ctypes.c_int32), ("partition", ctypes.c_int32), ("reverse_order", ctypes.c_int32),
+        ("receive", ctypes.c_int32),
     ]
 
 
@@ -150,10 +153,11 @@ def step_desc(batch, heads_q, heads_kv, head_dim, q_len, kv_len, dtype=BF16, cau
 
 
 def ring_desc(batch, heads_q, heads_kv, head_dim, local_len, world, rank, partition="zigzag",
-              dtype=BF16, causal=True, scale=0.0, reverse_order=False) -> RingDesc:
+              dtype=BF16, causal=True, scale=0.0, reverse_order=False, receive="auto") -> RingDesc:
     part = PARTITIONS[partition] if isinstance(partition, str) else int(partition)
+    recv = RECEIVES[receive] if isinstance(receive, str) else int(receive)
     return RingDesc(batch, heads_q, heads_kv, head_dim, local_len, dtype, int(causal), scale, world,
-                    rank, part, int(reverse_order))
+                    rank, part, int(reverse_order), recv)
 
 
 def partition_segments(partition, world: int, rank: int, local_len: int):

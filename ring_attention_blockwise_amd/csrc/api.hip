@@ -203,6 +203,8 @@ int check_ring_desc(const ra_ring_desc* d) {
     return fail(RA_ERR_INVALID_ARG, "zigzag needs an even local_len");
   if (d->reverse_order != 0 && d->reverse_order != 1) return fail(RA_ERR_INVALID_ARG, "reverse_order must be 0/1");
   if (d->causal != 0 && d->causal != 1) return fail(RA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (d->receive < RA_RECV_AUTO || d->receive > RA_RECV_FUSED)
+    return fail(RA_ERR_INVALID_ARG, "unknown receive %d", d->receive);
   ra_step_desc s{};
   s.batch = d->batch;
   s.heads_q = d->heads_q;
@@ -213,6 +215,14 @@ int check_ring_desc(const ra_ring_desc* d) {
   s.dtype = d->dtype;
   s.scale = d->scale;
   return check_shape(&s, true);
+}
+
+// The receive of one block (K and V, `bytes` each) into a slot on stream xs.
+hipError_t receive_block(void* dst_k, const void* src_k, void* dst_v, const void* src_v, size_t bytes,
+                         hipStream_t xs) {
+  hipError_t e = hipMemcpyAsync(dst_k, src_k, bytes, hipMemcpyDeviceToDevice, xs);
+  if (e != hipSuccess) return e;
+  return hipMemcpyAsync(dst_v, src_v, bytes, hipMemcpyDeviceToDevice, xs);
 }
 
 int32_t owner_of(const ra_ring_desc* d, int32_t step) {
@@ -444,6 +454,10 @@ int forward_run(const ra_ring_desc* d, const RingLayout& L, const void* q_local,
   float* m = reinterpret_cast<float*>(base + L.off_m);
   float* l = reinterpret_cast<float*>(base + L.off_l);
 
+  // Fused receive: the block of step s+1 is copied by step s's kernel when
+  // step s launches one; the other receives go on the compute stream.
+  const bool fused = d->dtype == RA_BF16 && (d->receive == RA_RECV_AUTO || d->receive == RA_RECV_FUSED);
+  if (fused) xs = cs;
   const bool two_streams = xs != cs;
   DriverEvents* ev = nullptr;
   hipError_t e;
@@ -466,18 +480,16 @@ int forward_run(const ra_ring_desc* d, const RingLayout& L, const void* q_local,
     hipError_t err;
     if (freed_recorded[slot] && two_streams)
       if ((err = hipStreamWaitEvent(xs, ev->freed[slot], 0)) != hipSuccess) return err;
-    if ((err = hipMemcpyAsync(slot_k[slot], k_blocks[owner[s]], L.block_bytes, hipMemcpyDeviceToDevice, xs)) !=
-        hipSuccess)
-      return err;
-    if ((err = hipMemcpyAsync(slot_v[slot], v_blocks[owner[s]], L.block_bytes, hipMemcpyDeviceToDevice, xs)) !=
-        hipSuccess)
+    if ((err = receive_block(slot_k[slot], k_blocks[owner[s]], slot_v[slot], v_blocks[owner[s]], L.block_bytes,
+                             xs)) != hipSuccess)
       return err;
     return two_streams ? hipEventRecord(ev->ready[slot], xs) : hipSuccess;
   };
 
   for (int s = 0; s < n; ++s) {
     // receive the block of step s+1 while step s computes
-    if (s + 1 < n)
+    const bool rx_in_step = fused && pairs[s] > 0 && s + 1 < n;
+    if (s + 1 < n && !rx_in_step)
       if ((e = enqueue_receive(s + 1)) != hipSuccess) return hip_fail(e, "receive copy");
     const void* kb = k_blocks[owner[s]];
     const void* vb = v_blocks[owner[s]];
@@ -502,6 +514,15 @@ int forward_run(const ra_ring_desc* d, const RingLayout& L, const void* q_local,
       a.final_ = (s == last);
       a.out = out;
       a.lse = lse;
+      if (rx_in_step) {
+        // slot (s+1)%2 was last read by step s-1, which is complete
+        const int slot = (s + 1) & 1;
+        a.rx_src[0] = k_blocks[owner[s + 1]];
+        a.rx_src[1] = v_blocks[owner[s + 1]];
+        a.rx_dst[0] = slot_k[slot];
+        a.rx_dst[1] = slot_v[slot];
+        a.rx_bytes = (int64_t)L.block_bytes;
+      }
       if ((e = launch_step(a, d->head_dim, d->dtype, cs)) != hipSuccess) return hip_fail(e, "step launch");
     }
     if (step_events)
@@ -927,11 +948,8 @@ int ring_attn_backward(const ra_ring_desc* d, const void* q_local, const void* c
     hipError_t err;
     if (freed_recorded[slot] && xs != cs)
       if ((err = hipStreamWaitEvent(xs, ev->freed[slot], 0)) != hipSuccess) return err;
-    if ((err = hipMemcpyAsync(slot_k[slot], k_blocks[owner[s]], L.block_bytes, hipMemcpyDeviceToDevice, xs)) !=
-        hipSuccess)
-      return err;
-    if ((err = hipMemcpyAsync(slot_v[slot], v_blocks[owner[s]], L.block_bytes, hipMemcpyDeviceToDevice, xs)) !=
-        hipSuccess)
+    if ((err = receive_block(slot_k[slot], k_blocks[owner[s]], slot_v[slot], v_blocks[owner[s]], L.block_bytes,
+                             xs)) != hipSuccess)
       return err;
     return hipEventRecord(ev->ready[slot], xs);
   };

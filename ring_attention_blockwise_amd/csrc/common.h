@@ -42,6 +42,16 @@ struct StepArgs {
   int32_t n_kv_seg;
   Seg qs[2];
   Seg ks[2];
+  // Fused receive (bf16 step only): while it computes, the launch also
+  // copies rx_bytes of each of two tensors, rx_src[i] -> rx_dst[i] (the next
+  // K/V block into its receive slot). Work items whose query tile is at or
+  // after rx_tile_lo take rx_share bytes of both tensors each, in the order
+  // of their dense rank. rx_bytes == 0: no receive in this launch.
+  const void* rx_src[2];
+  void* rx_dst[2];
+  int64_t rx_bytes;
+  int64_t rx_share;
+  int32_t rx_tile_lo;
 };
 
 // The lazy-rescale threshold in base-2 exponent units: the reference m is
@@ -58,6 +68,7 @@ hipError_t launch_finalize(const float* o, const float* m, const float* l, void*
                            int64_t rows, int head_dim, int dtype, hipStream_t s);
 hipError_t launch_init_state(float* o, float* m, float* l, int64_t rows, int head_dim,
                              hipStream_t s);
+
 
 // ---- device helpers shared by the finalize kernel and the fused finalize of
 // the step kernels (so both produce bit-identical results). ----------------
@@ -95,14 +106,14 @@ __device__ __forceinline__ int64_t seg_position(const Seg* segs, int n, int64_t 
 }
 
 // Number of entries of `s` whose position is <= x.
-__device__ __forceinline__ int64_t seg_count_le(const Seg& s, int64_t x) {
+__host__ __device__ __forceinline__ int64_t seg_count_le(const Seg& s, int64_t x) {
   if (x < s.start) return 0;
   const int64_t c = (x - s.start) / s.stride + 1;
   return c < s.len ? c : s.len;
 }
 
 // Position range of local rows [r0, r1) (r1 > r0) under the segments.
-__device__ __forceinline__ void seg_range(const Seg* segs, int n, int64_t r0, int64_t r1, int64_t* lo,
+__host__ __device__ __forceinline__ void seg_range(const Seg* segs, int n, int64_t r0, int64_t r1, int64_t* lo,
                                           int64_t* hi) {
   if (n <= 0) {
     *lo = r0;
@@ -147,7 +158,7 @@ struct TilePlan {
   KeyRange r0;
   KeyRange r1;
   int32_t n;
-  __device__ __forceinline__ int32_t total_tiles() const {
+  __host__ __device__ __forceinline__ int32_t total_tiles() const {
     return (n > 0 ? r0.ntiles : 0) + (n > 1 ? r1.ntiles : 0);
   }
   // range of tile t and the tile's first local key
@@ -155,7 +166,7 @@ struct TilePlan {
 };
 
 template <int BN>
-__device__ __forceinline__ KeyRange make_range(const Seg& g, int32_t seg, int64_t off, int64_t qmin, int64_t qmax) {
+__host__ __device__ __forceinline__ KeyRange make_range(const Seg& g, int32_t seg, int64_t off, int64_t qmin, int64_t qmax) {
   const int64_t vis = seg_count_le(g, qmax);
   const int64_t full = seg_count_le(g, qmin);
   KeyRange r;
@@ -169,7 +180,7 @@ __device__ __forceinline__ KeyRange make_range(const Seg& g, int32_t seg, int64_
 }
 
 template <int BN>
-__device__ __forceinline__ TilePlan plan_tiles(const StepArgs& a, int64_t qmin, int64_t qmax) {
+__host__ __device__ __forceinline__ TilePlan plan_tiles(const StepArgs& a, int64_t qmin, int64_t qmax) {
   TilePlan p;
   p.n = 0;
   p.r0 = KeyRange{0, 0, 0, 0, 0, -1};

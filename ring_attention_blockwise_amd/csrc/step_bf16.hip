@@ -34,6 +34,14 @@
 //    path of iteration t).
 //  * LDS layout, swizzle, operand lane layouts and the transposed V reads are
 //    those of bf16_tiles.h.
+//  * Fused receive (optional): the launch also copies the next ring block
+//    into its receive slot. Each work item takes a share of it, in pieces of
+//    1 KB per wave, spread evenly over its iterations: in a receive
+//    iteration every wave requests its next piece (buffer-to-LDS into a
+//    private staging ring of three 1 KB slots) and stores the piece it
+//    requested two receive iterations earlier from LDS to the slot. A
+//    receive iteration leaves its fetch in flight at the barrier wait as
+//    well; what the iterations do not cover is copied after the loop.
 #include <type_traits>
 
 #include "bf16_tiles.h"
@@ -58,6 +66,13 @@ constexpr int kAhead = RA_PIPE_AHEAD;  // MFMAs whose LDS operands are in flight
 // 1 KB copies per wave for one K (or V) tile
 template <int D>
 constexpr int kCopies = Layout<D>::kTileBytes / 1024 / kWaves;
+
+// Fused receive: a piece is 1 KB per wave, 8 KB per workgroup; three staging
+// slots per wave after the K/V rings.
+constexpr int kRxPiece = kWaves * 1024;
+constexpr int kRxSlots = 3;
+constexpr int kRxStageBytes = kRxSlots * kRxPiece;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Copies of one tensor (K or V) of one head into the LDS rings. Set up once
 // per work item: the head's base address in SGPRs and this lane's byte
@@ -126,7 +141,7 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
   using Ly = Layout<D>;
   constexpr int NP = 4 * Ly::kDBlocks;  // P-V products per tile
   constexpr int NS = 2 * Ly::kDChunks;  // S products per tile
-  __shared__ __attribute__((aligned(1024))) char smem[Ly::kSmemBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[Ly::kSmemBytes + kRxStageBytes];
 
   // ---- work item ------------------------------------------------------------
   // Workgroup i runs on XCD i % 8. When the (batch, KV head) pairs divide
@@ -134,9 +149,13 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
   // their K/V), heavy (late) causal tiles first. Otherwise (e.g. one KV head)
   // that would hand the heavy tiles to some XCDs and the light ones to
   // others, so the heavy-first order is dealt round-robin over all XCDs.
+  // Items whose tile is at or after rx_tile_lo carry a share of the fused
+  // receive; rx_rank is their dense rank (-1: no share).
   int32_t tile, b, h;
+  int64_t rx_rank = -1;
   {
     const int32_t n_bk = a.batch * a.heads_kv;
+    const int32_t rx_tiles = q_tiles - a.rx_tile_lo;
     if (n_bk % 8 == 0) {
       const int32_t item = (int32_t)(blockIdx.x % 8) * items_per_xcd + (int32_t)(blockIdx.x / 8);
       if (item >= n_items) return;
@@ -146,6 +165,7 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
       tile = q_tiles - 1 - rem / a.group;
       b = bk / a.heads_kv;
       h = (bk % a.heads_kv) * a.group + rem % a.group;
+      if (a.rx_bytes > 0 && rem < rx_tiles * a.group) rx_rank = (int64_t)bk * rx_tiles * a.group + rem;
     } else {
       const int32_t item = (int32_t)blockIdx.x;
       if (item >= n_items) return;
@@ -153,6 +173,7 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
       tile = q_tiles - 1 - item / n_bh;
       b = (item % n_bh) / a.heads_q;
       h = (item % n_bh) % a.heads_q;
+      if (a.rx_bytes > 0 && item < rx_tiles * n_bh) rx_rank = item;
     }
   }
   const int32_t kvh = h / a.group;
@@ -163,13 +184,55 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
   const int qcol = lane & 31;
   const int hh = lane >> 5;
 
+  // ---- fused receive: this item's share [rx_lo, rx_lo + rx_len) of each of
+  // the two tensors, in pieces j = 0 .. n_rx-1 (tensor j % 2, 8 KB piece j / 2;
+  // the wave moves its KB of each) ----------------------------------------------
+  int64_t rx_lo = 0, rx_len = 0;
+  if (rx_rank >= 0) {
+    rx_lo = rx_rank * a.rx_share < a.rx_bytes ? rx_rank * a.rx_share : a.rx_bytes;
+    rx_len = a.rx_bytes - rx_lo < a.rx_share ? a.rx_bytes - rx_lo : a.rx_share;
+  }
+  const int32_t n_rx = 2 * (int32_t)((rx_len + kRxPiece - 1) / kRxPiece);
+  // Wave-uniform addresses of this wave's first KB of the share in each
+  // source and destination tensor, and the share's bytes from there on (a
+  // share is far below 2 GB).
+  const uint64_t rx_wave = (uint64_t)(rx_lo + wave * 1024);
+  const uint64_t rx_s0 = uniform_address(a.rx_src[0]) + rx_wave;
+  const uint64_t rx_s1 = uniform_address(a.rx_src[1]) + rx_wave;
+  const uint64_t rx_d0 = uniform_address(a.rx_dst[0]) + rx_wave;
+  const uint64_t rx_d1 = uniform_address(a.rx_dst[1]) + rx_wave;
+  const int32_t rx_left = (int32_t)rx_len - wave * 1024;
+  // Piece j of this wave: byte offset from the wave's first KB and length
+  // (0 outside the share).
+  auto rx_piece = [&](int32_t j, int32_t& off, int32_t& nbytes) {
+    const int32_t o = (j >> 1) * kRxPiece;
+    const int32_t left = rx_left - o;
+    const bool in = j >= 0 && j < n_rx && left > 0;
+    off = in ? o : 0;
+    nbytes = in ? (left < 1024 ? left : 1024) : 0;
+  };
+  // The pieces [j0, n_rx) with plain loads and stores (after the loop, or
+  // for an item with no key tile).
+  auto rx_direct = [&](int32_t j0) {
+    for (int32_t j = j0 < 0 ? 0 : j0; j < n_rx; ++j) {
+      int32_t off, nb;
+      rx_piece(j, off, nb);
+      const uint64_t src = ((j & 1) ? rx_s1 : rx_s0) + (uint64_t)(off + lane * 16);
+      const uint64_t dst = ((j & 1) ? rx_d1 : rx_d0) + (uint64_t)(off + lane * 16);
+      if (lane * 16 < nb) *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+    }
+  };
+
   const int64_t row0 = (int64_t)tile * kBM;
   const int64_t r1 = (row0 + kBM < a.q_len) ? row0 + kBM : a.q_len;
   int64_t qmin, qmax;
   seg_range(a.qs, a.n_q_seg, row0, r1, &qmin, &qmax);
   const TilePlan plan = plan_tiles<kBN>(a, qmin, qmax);
   const int ntiles = plan.total_tiles();
-  if (ntiles == 0 && !a.init && !a.final_) return;  // nothing visible, state untouched
+  if (ntiles == 0 && !a.init && !a.final_) {  // nothing visible, state untouched
+    rx_direct(0);
+    return;
+  }
 
   const int64_t row = row0 + wave * 32 + qcol;
   const bool valid = row < a.q_len;
@@ -196,6 +259,25 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
     vcopy.copy(a.kv_len, tile_start(t), t < ntiles, smem_base + Ly::kVBase + (uint32_t)(t % kStages) * Ly::kTileBytes,
                wave);
   };
+  // Piece j into staging slot `slot` (buffer-to-LDS), and the piece held in
+  // staging out to the receive slot as piece j. Outside the share both use
+  // empty buffer ranges: the fetch fills the staging slot with zeros, the
+  // store writes nothing.
+  const uint32_t rx_stage = smem_base + Ly::kSmemBytes + (uint32_t)wave * 1024u;
+  const int rx_voff[1] = {lane * 16};
+  auto rx_fetch = [&](int32_t j, uint32_t slot) {
+    int32_t off, nb;
+    rx_piece(j, off, nb);
+    dma16_blocks<1>(resource_at((j & 1) ? rx_s1 : rx_s0, (uint64_t)off, nb), rx_stage + slot * kRxPiece, rx_voff);
+  };
+  auto rx_put = [&](int32_t j, const u32x4& x) {
+    int32_t off, nb;
+    rx_piece(j, off, nb);
+    void* dst = reinterpret_cast<void*>(((j & 1) ? rx_d1 : rx_d0) + (uint64_t)off);
+    __builtin_amdgcn_raw_buffer_store_b128(x, __builtin_amdgcn_make_buffer_rsrc(dst, 0, nb, kBufferWord3), lane * 16,
+                                           0, 0);
+  };
+
   // K of tiles 0 and 1 and V of tile 0 first (iteration 0 reads them), and
   // zeros into the V stage of "tile -1" (the stage of tile 3, requested in
   // iteration 1)
@@ -347,12 +429,29 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
   // iteration t+1 reads, then publish them: K of t+2 (its S products,
   // requested at the start of iteration t-1) and V of t+1 (read at the end
   // of iteration t+1 for the first P-V products of iteration t+2, requested
-  // in the middle of iteration t-1). The two copy groups issued since (K of
-  // t+3, V of t+2: a fixed number, empty tiles included) may stay in flight.
-  auto publish = [&]() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kCopies<D>) : "memory");
+  // in the middle of iteration t-1). The loads issued after V of t+1 may
+  // stay in flight: K of t+3, in a receive iteration the fetch of one piece,
+  // and V of t+2. The counter also counts stores, and a store may be
+  // counted done before older loads, so stores are never part of the
+  // allowance: a store still in flight only makes the wait stricter. The
+  // receive fetches of earlier iterations are older than V of t+1, so they
+  // have landed too.
+  auto publish = [&](bool rx_on) {
+    if (rx_on)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kCopies<D> + 1) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kCopies<D>) : "memory");
     asm volatile("s_barrier" ::: "memory");
   };
+
+  // Receive iterations: every rx_every-th iteration while pieces are left,
+  // plus two to store the last two; only the first iteration of each group
+  // of four (the unrolled loop body) can be one, so rx_every is a multiple
+  // of 4 and the other three carry no receive code. rx_r counts them,
+  // rx_slot is the staging slot of piece rx_r (rx_r mod 3).
+  const int32_t rx_every = 4 * (4 * (n_rx + 2) <= ntiles ? ntiles / (4 * (n_rx + 2)) : 1);
+  int32_t rx_r = 0, rx_next = 0;
+  uint32_t rx_slot = 0;
 
   // One iteration t with K of tile t+1 in stage SK and V of tile t-1 in
   // stage SV; the softmax tile is sacc[BUF], the next S goes to
@@ -361,7 +460,7 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
   // "tile -1" are zero and its V stage holds zeros, so those products add
   // nothing; for the last tile the S products read a stage of zeros and are
   // never used.
-  auto iteration = [&](auto sk_tag, auto sv_tag, auto buf_tag, int t) {
+  auto iteration = [&](auto sk_tag, auto sv_tag, auto buf_tag, auto rx_tag, int t) {
     constexpr int SK = decltype(sk_tag)::value;
     constexpr int SV = decltype(sv_tag)::value;
     constexpr int BUF = decltype(buf_tag)::value;
@@ -370,6 +469,12 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
     // K of tile t+3 goes to the stage of K of tile t-1 (last read before the
     // previous barrier)
     issue_k(t + kKAhead);
+    // receive: fetch piece r, store piece r-2 (from the slot after r's)
+    const bool rx_on = decltype(rx_tag)::value && t == rx_next && rx_r < n_rx + 2;
+    const int32_t r = rx_r;
+    const uint32_t slot_in = rx_slot;
+    const uint32_t slot_out = rx_slot == kRxSlots - 1 ? 0u : rx_slot + 1;
+    if (rx_on) rx_fetch(r, slot_in);
     mask_tile(sacc[BUF], t);
     const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
     f32x16(&sc)[2] = sacc[BUF];
@@ -398,6 +503,7 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
     float p[32];
     float part[4];
     float mx = sc[0][0];
+    u32x4 rx_x;
     bf16x2 pairs[16];
     auto elem = [&](int e) -> float { return sc[e / 16][e % 16]; };
 #pragma unroll
@@ -415,6 +521,8 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
         sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[k], qf[c], c == 0 ? zero : sn[kb], 0, 0, 0);
       }
       if (k + kAhead < NM) read_operand(k + kAhead);
+      if (k == 0 && rx_on) rx_x = *lds_ptr<u32x4>(rx_stage + slot_out * kRxPiece + lane * 16);
+      if (k == 2 && rx_on) rx_put(r - 2, rx_x);
 #pragma unroll
       for (int e = k * EPS; e < (k + 1) * EPS; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(elem(e), sl2, -msub));
       if (k >= 1) {
@@ -463,7 +571,12 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
     // (for t = 0, by the barrier before the loop)
 #pragma unroll
     for (int k = 0; k < kPre; ++k) vpre[k] = read_vt<D, (SV + 1) % 4>(k, v_addr);
-    publish();
+    publish(rx_on);
+    if (rx_on) {
+      ++rx_r;
+      rx_next += rx_every;
+      rx_slot = slot_out;
+    }
   };
 
   // The P-V products of the last tile (V in stage SV, weights in pf[BUF]).
@@ -490,13 +603,13 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
     for (int k = 0; k < kPre; ++k) vpre[k] = read_vt<D, 3>(k, v_addr);  // "tile -1": zeros
     // iteration t: K of t+1 in stage (t+1)%4, V of t-1 in (t-1)%4, buffer t%2
     for (int t = 0; t < ntiles; t += 4) {
-      iteration(I1{}, I3{}, I0{}, t);
+      iteration(I1{}, I3{}, I0{}, std::true_type{}, t);
       if (t + 1 >= ntiles) break;
-      iteration(I2{}, I0{}, I1{}, t + 1);
+      iteration(I2{}, I0{}, I1{}, std::false_type{}, t + 1);
       if (t + 2 >= ntiles) break;
-      iteration(I3{}, I1{}, I0{}, t + 2);
+      iteration(I3{}, I1{}, I0{}, std::false_type{}, t + 2);
       if (t + 3 >= ntiles) break;
-      iteration(I0{}, I2{}, I1{}, t + 3);
+      iteration(I0{}, I2{}, I1{}, std::false_type{}, t + 3);
     }
     switch ((ntiles - 1) & 3) {  // P-V of the last tile
       case 0: last_pv(I0{}, I0{}); break;
@@ -505,6 +618,10 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
       default: last_pv(I3{}, I1{}); break;
     }
   }
+
+  // receive pieces the loop did not store (piece r-2 is stored in receive
+  // iteration r)
+  rx_direct(rx_r - 2);
 
   // ---- write back ---------------------------------------------------------------
   const float l_tot = sum_with_partner(l_run);
@@ -544,11 +661,40 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
 
 }  // namespace
 
-hipError_t launch_step_bf16(const StepArgs& a, int head_dim, hipStream_t s) {
-  const int64_t q_tiles = (a.q_len + kBM - 1) / kBM;
-  const int64_t items = q_tiles * a.heads_q * a.batch;
+hipError_t launch_step_bf16(const StepArgs& args, int head_dim, hipStream_t s) {
+  const int64_t q_tiles = (args.q_len + kBM - 1) / kBM;
+  const int64_t items = q_tiles * args.heads_q * args.batch;
   const int64_t per_xcd = (items + 7) / 8;
   const dim3 grid((unsigned)(per_xcd * 8));
+  StepArgs a = args;
+  if (a.rx_bytes > 0) {
+    // Carriers of the receive: the items of query tiles lo .. q_tiles-1,
+    // each taking rx_share bytes of both tensors, i.e. n = 2 * rx_share / 8 KB
+    // pieces, moved in n + 2 receive iterations at most one in four
+    // iterations apart. Take the lowest lo for which every carrier has
+    // enough key tiles to move its pieces inside its loop (the late tiles
+    // of the causal layouts see the most keys); failing that, every item
+    // carries and the rest is copied after the loop.
+    auto share_of = [&](int64_t lo) {
+      const int64_t carriers = (q_tiles - lo) * a.heads_q * a.batch;
+      const int64_t per = (a.rx_bytes + carriers - 1) / carriers;
+      return (per + kRxPiece - 1) / kRxPiece * kRxPiece;
+    };
+    int64_t best = -1;
+    int64_t min_tiles = INT64_MAX;
+    for (int64_t lo = q_tiles - 1; lo >= 0 && min_tiles >= 16; --lo) {  // a carrier needs >= 16 tiles
+      const int64_t r0 = lo * kBM;
+      const int64_t r1 = r0 + kBM < a.q_len ? r0 + kBM : a.q_len;
+      int64_t qmin, qmax;
+      seg_range(a.qs, a.n_q_seg, r0, r1, &qmin, &qmax);
+      const int64_t nt = plan_tiles<kBN>(a, qmin, qmax).total_tiles();
+      min_tiles = nt < min_tiles ? nt : min_tiles;
+      if (min_tiles >= 4 * (2 * (share_of(lo) / kRxPiece) + 2)) best = lo;
+    }
+    if (best < 0) best = 0;
+    a.rx_tile_lo = (int32_t)best;
+    a.rx_share = share_of(best);
+  }
   if (head_dim == 128)
     step_bf16_kernel<128><<<grid, kThreads, 0, s>>>(a, (int32_t)items, (int32_t)per_xcd, (int32_t)q_tiles);
   else

@@ -37,9 +37,10 @@ def torch_dtype(wl):
     return torch.bfloat16 if wl.dtype == "bf16" else torch.float32
 
 
-def make_ring_desc(wl: ring_inputs.Workload, rank: int, reverse_order: bool = False) -> RingDesc:
+def make_ring_desc(wl: ring_inputs.Workload, rank: int, reverse_order: bool = False, receive="auto") -> RingDesc:
     return ring_desc(wl.batch, wl.heads_q, wl.heads_kv, wl.head_dim, wl.local_len, wl.world, rank,
-                     wl.partition, dtype=dtype_code(wl), causal=wl.causal, reverse_order=reverse_order)
+                     wl.partition, dtype=dtype_code(wl), causal=wl.causal, reverse_order=reverse_order,
+                     receive=receive)
 
 
 @dataclasses.dataclass
@@ -51,8 +52,8 @@ class DeviceShare:
     v_blocks: list
     q_positions: np.ndarray     # global position of each local row
 
-    def ring_desc(self, reverse_order=False) -> RingDesc:
-        return make_ring_desc(self.workload, self.rank, reverse_order)
+    def ring_desc(self, reverse_order=False, receive="auto") -> RingDesc:
+        return make_ring_desc(self.workload, self.rank, reverse_order, receive)
 
 
 def _to_device(x: np.ndarray, dt, device):
@@ -132,13 +133,14 @@ def alloc_workspace(share: DeviceShare, reverse_order=False):
 
 
 def run_forward(share: DeviceShare, reverse_order=False, copy_stream=None, workspace=None, out=None, lse=None,
-                step_events=None):
-    """ring_attn_forward on the current stream (receive copies on ``copy_stream``)."""
+                step_events=None, receive="auto"):
+    """ring_attn_forward on the current stream (receive copies on ``copy_stream``,
+    made as ``receive`` says: "auto", "memcpy" or "fused")."""
     if out is None:
         out, lse = alloc_outputs(share)
     if workspace is None:
         workspace = alloc_workspace(share, reverse_order)
-    forward(share.ring_desc(reverse_order), share.q, share.k_blocks, share.v_blocks, out, lse, workspace,
+    forward(share.ring_desc(reverse_order, receive), share.q, share.k_blocks, share.v_blocks, out, lse, workspace,
             copy_stream=copy_stream, step_events=step_events)
     return out, lse
 
@@ -205,10 +207,10 @@ def new_kv_grads(share: DeviceShare):
 
 
 def run_backward(share: DeviceShare, out, lse, d_out, dk_acc, dv_acc, copy_stream=None, workspace=None,
-                 step_events=None):
+                 step_events=None, receive="auto"):
     """ring_attn_backward on the current stream; returns dQ (input dtype)."""
     import torch
-    rd = share.ring_desc()
+    rd = share.ring_desc(receive=receive)
     if workspace is None:
         workspace = torch.empty(backward_workspace_size(rd), dtype=torch.uint8, device=share.q.device)
     dq = torch.empty_like(share.q)

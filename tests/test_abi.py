@@ -158,6 +158,13 @@ def test_forward_rejects_small_workspace_and_bad_desc():
                                None) == ra.ERR_INVALID_ARG
     bad = ra.ring_desc(1, 2, 1, 64, 16, 4, 4)                      # rank out of range
     assert ra.lib().ring_attn_forward_workspace_size(ctypes.byref(bad)) == 0
+    for recv in (-1, 3):                                           # unknown receive mode
+        bad = ra.ring_desc(1, 2, 1, 64, 16, 4, 0, receive=recv)
+        assert ra.lib().ring_attn_forward_workspace_size(ctypes.byref(bad)) == 0
+        assert L.ring_attn_forward(ctypes.byref(bad), FAKE, blocks, blocks, FAKE, FAKE, FAKE, ws, None, None,
+                                   None) == ra.ERR_INVALID_ARG
+    for recv in ("auto", "memcpy", "fused"):
+        assert ra.forward_workspace_size(ra.ring_desc(1, 2, 1, 64, 16, 4, 0, receive=recv)) == ws
     nulls = (ctypes.c_void_p * 4)(*([0x10000] * 3 + [None]))
     assert L.ring_attn_forward(ctypes.byref(rd), FAKE, blocks, nulls, FAKE, FAKE, FAKE, ws, None, None,
                                None) == ra.ERR_INVALID_ARG

@@ -4,9 +4,10 @@ manual loop of ring_attn_step + ring_attn_finalize (bitwise), any ring
 order, resume from a host copy of the state, determinism.
 
 Small workloads compare every row. The full-size workloads run in exactly
-the configuration the benchmark times (ring_attn_forward with the receive
-copies on a side stream) and compare a seeded sample of rows that always
-includes tile and chunk boundaries, over all heads, with the oracle."""
+the configuration the benchmark times (ring_attn_forward with its default
+receive, done inside the step kernels) and compare a seeded sample of rows
+that always includes tile and chunk boundaries, over all heads, with the
+oracle. The receive modes give the same bits."""
 import numpy as np
 import pytest
 
@@ -71,13 +72,55 @@ def test_forward_equals_manual_loop_bitwise(gpu, name):
     import torch
     wl = W[name]
     share = harness.build_share(wl, 0, gpu)
-    out_f, lse_f = harness.run_forward(share, copy_stream=_copy_stream())
-    out_s, lse_s = harness.run_forward(share, copy_stream=None)      # receive on the compute stream
+    out_f, lse_f = harness.run_forward(share, copy_stream=_copy_stream())  # default receive
+    out_c, lse_c = harness.run_forward(share, copy_stream=_copy_stream(), receive="memcpy")
+    out_s, lse_s = harness.run_forward(share, copy_stream=None, receive="memcpy")  # on the compute stream
     st = harness.run_steps(share, range(wl.world))
     out_m, lse_m = harness.finalize_state(share, st)
     torch.cuda.synchronize()
-    assert torch.equal(out_f, out_m) and torch.equal(lse_f, lse_m)
-    assert torch.equal(out_f, out_s) and torch.equal(lse_f, lse_s)
+    for o, s in ((out_f, lse_f), (out_c, lse_c), (out_s, lse_s)):
+        assert torch.equal(o, out_m) and torch.equal(s, lse_m)
+
+
+# Shares for the fused receive: the full-size ones the benchmark times, a
+# contiguous device whose later blocks are fully masked (no kernel: those
+# receives fall back to a copy), and small ragged shares whose receive does
+# not fill the last 8 KB piece or outlasts the key tiles of some work items.
+_RECEIVE_CASES = [
+    ("zigzag128k_8dev_gqa", 0, {}),
+    ("zigzag1m_64dev", 0, {}),
+    ("contig1m_64dev", 63, {}),
+    ("contig1m_64dev", 5, {}),
+    ("striped128k_8dev_gqa", 5, {}),
+    ("stress256k_8dev_d64", 7, {}),
+    ("zigzag8k_8dev_d128", 3, {}),
+    ("zigzag8k_8dev_d128", 1, dict(heads_q=6, heads_kv=3, world=4, local_len=520)),
+    ("zigzag8k_8dev_d128", 2, dict(heads_q=2, heads_kv=1, world=3, local_len=96, head_dim=64)),
+    ("zigzag8k_8dev_d128", 0, dict(heads_q=4, heads_kv=4, world=2, local_len=2, causal=False)),
+]
+
+
+@pytest.mark.parametrize("name,rank,kw", _RECEIVE_CASES)
+def test_fused_receive_equals_copy_bitwise(gpu, name, rank, kw):
+    """The receive done inside the step kernels gives the same bits as
+    hipMemcpyAsync on a side stream. The workspace starts as all-ones bytes
+    (bf16 NaN) each time, so a piece of a block the fused receive missed
+    shows up as a NaN or a changed value."""
+    import torch
+    wl = W[name].with_(**kw) if kw else W[name]
+    print(f"{name} rank {rank} {kw}", flush=True)
+    share = harness.build_share(wl, rank, gpu)
+    ws = harness.alloc_workspace(share)
+    res = {}
+    for mode, cs in (("fused", None), ("memcpy", _copy_stream()), ("fused", _copy_stream())):
+        ws.fill_(255)
+        out, lse = harness.run_forward(share, copy_stream=cs, workspace=ws, receive=mode)
+        torch.cuda.synchronize()
+        res.setdefault(mode, []).append((out.clone(), lse.clone()))
+    ref_o, ref_l = res["memcpy"][0]
+    assert torch.isfinite(ref_o.float()).all()
+    for o, s in res["fused"]:
+        assert torch.equal(o, ref_o) and torch.equal(s, ref_l)
 
 
 def test_ring_order_invariance(gpu):
@@ -147,11 +190,11 @@ def test_release_thread_events_then_forward_again(gpu):
     wl = W["zigzag8k_8dev_d128"]
     share = harness.build_share(wl, 1, gpu)
     cs = _copy_stream()
-    a = [x.clone() for x in harness.run_forward(share, copy_stream=cs)]
+    a = [x.clone() for x in harness.run_forward(share, copy_stream=cs, receive="memcpy")]
     torch.cuda.synchronize()
     ra.release_thread_events()
     ra.release_thread_events()  # nothing left to destroy
-    b = harness.run_forward(share, copy_stream=cs)
+    b = harness.run_forward(share, copy_stream=cs, receive="memcpy")
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
