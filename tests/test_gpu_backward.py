@@ -139,6 +139,29 @@ def test_backward_is_deterministic_and_accumulates(gpu):
         assert torch.equal(2 * dk1[j], dk2[j]) and torch.equal(2 * dv1[j], dv2[j])
 
 
+@pytest.mark.parametrize("name,rank", [("stress256k_8dev_d64", 7), ("zigzag128k_8dev_gqa", 0)])
+def test_full_size_backward_is_deterministic(gpu, name, rank):
+    """Repeated backward passes of a full-size share give the same bits in
+    every row of dQ, dK and dV (a tile read before every wave's copy of it
+    has landed would make some rows change from run to run)."""
+    import torch
+    wl = ring_inputs.WORKLOADS[name]
+    share = harness.build_share(wl, rank, gpu)
+    out, lse = harness.run_forward(share)
+    d_out = harness.build_upstream(share)
+    ref = None
+    for rep in range(4):
+        dk, dv = harness.new_kv_grads(share)
+        dq = harness.run_backward(share, out, lse, d_out, dk, dv, copy_stream=_copy_stream())
+        torch.cuda.synchronize()
+        if ref is None:
+            ref = (dq.clone(), [x.clone() for x in dk], [x.clone() for x in dv])
+            continue
+        assert torch.equal(dq, ref[0])
+        assert all(torch.equal(a, b) for a, b in zip(dk, ref[1]))
+        assert all(torch.equal(a, b) for a, b in zip(dv, ref[2]))
+
+
 KEY_WINDOW = 1024      # sampled keys sit in the last KEY_WINDOW global positions
 KEYS_PER_HEAD = 64
 DQ_ROWS = 256
