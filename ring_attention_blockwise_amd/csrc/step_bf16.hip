@@ -17,11 +17,13 @@
 //    same iteration, so the matrix pipe and the vector ALU of a SIMD run side
 //    by side in both of its waves.
 //  * The exponentials of tile t are taken against the current reference
-//    maximum before the tile's maximum is known. The reference is raised only
-//    when a row's maximum passes it by more than 8 in base-2 units (so every
-//    weight stays <= 2^8); in that rare case (always on a row's first tile)
-//    the tile's weights are recomputed against the new reference and O, l
-//    are rescaled, off the main path.
+//    maximum, and the tile's maximum is not computed on the main path: a
+//    weight can exceed 2^8 only if the lane's sum of the tile's weights does,
+//    so that sum (needed for l anyway) decides. Only then, or on a row's
+//    first visible tile, the rare path recomputes the tile's scores, takes
+//    their maximum, raises the reference where the maximum passes it by more
+//    than 8 in base-2 units (so every weight stays <= 2^8), rescales O and l,
+//    and recomputes the weights (identical ones where nothing was raised).
 //  * K and V tiles are copied HBM -> LDS by 16-byte buffer-to-LDS loads into
 //    two rings of four stages each: K of tile t+3 at the start of iteration
 //    t, V of tile t+2 in its middle (every wave copies one eighth of each),
@@ -72,6 +74,10 @@ constexpr int kCopies = Layout<D>::kTileBytes / 1024 / kWaves;
 constexpr int kRxPiece = kWaves * 1024;
 constexpr int kRxSlots = 3;
 constexpr int kRxStageBytes = kRxSlots * kRxPiece;
+
+// A lane's speculative weights of one tile sum past this only if one of them
+// may exceed 2^kRescaleThreshold (each is >= 0).
+constexpr float kWeightCap = 256.0f;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Copies of one tensor (K or V) of one head into the LDS rings. Set up once
@@ -406,10 +412,21 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
   // by more than the threshold, rescale O and l, and recompute the tile's
   // scores and weights. O must already hold the products of tile t-1 (the
   // compiler orders the rescale after them).
-  auto settle = [&](auto st_tag, f32x16 (&s)[2], int t, float mx, float& psum, bf16x8 (&pb)[2][2]) {
-    const float cand = fmaxf(m_run, mx);
-    const bool need = cand > m_run + kRescaleThreshold;
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+  auto settle = [&](auto st_tag, f32x16 (&s)[2], int t, float& psum, bf16x8 (&pb)[2][2]) {
+    // Every speculative weight is <= 2^8 unless this lane's sum of them
+    // passed 2^8 (or overflowed): only then, or while the row has no
+    // reference yet (its first visible tile), is the tile's maximum needed.
+    if (__builtin_amdgcn_ballot_w64(!(psum <= kWeightCap) || m_run == -INFINITY) != 0) {
+      scores(st_tag, s);
+      mask_tile(s, t);
+      float mx = s[0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][j]);
+      mx = max_with_partner(mx) * sl2;
+      const float cand = fmaxf(m_run, mx);
+      const bool need = cand > m_run + kRescaleThreshold;
       const float m_upd = need ? cand : m_run;
       const float alpha = (m_upd == m_run) ? 1.0f : exp2f(m_run - m_upd);
 #pragma unroll
@@ -418,8 +435,6 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
         for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
       l_run *= alpha;
       m_run = m_upd;
-      scores(st_tag, s);
-      mask_tile(s, t);
       psum = weights(s, (m_run == -INFINITY) ? 0.0f : m_run, pb);
     }
     l_run += psum;
@@ -502,7 +517,6 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
     };
     float p[32];
     float part[4];
-    float mx = sc[0][0];
     u32x4 rx_x;
     bf16x2 pairs[16];
     auto elem = [&](int e) -> float { return sc[e / 16][e % 16]; };
@@ -529,7 +543,6 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
 #pragma unroll
         for (int e = (k - 1) * EPS; e < k * EPS; ++e) part[e & 3] = e < 4 ? p[e] : part[e & 3] + p[e];
       }
-      if (k < 16) mx = fmaxf(fmaxf(mx, elem(2 * k)), elem(2 * k + 1));
 #pragma unroll
       for (int m = 0; m < 16; ++m)
         if ((2 * m + 1) / EPS + 2 == k) pairs[m] = __builtin_convertvector((f32x2){p[2 * m], p[2 * m + 1]}, bf16x2);
@@ -541,10 +554,6 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
 #pragma unroll
     for (int m = 0; m < 16; ++m)
       if ((2 * m + 1) / EPS + 2 >= NM) pairs[m] = __builtin_convertvector((f32x2){p[2 * m], p[2 * m + 1]}, bf16x2);
-    if (NM < 16) {
-#pragma unroll
-      for (int k = NM; k < 16; ++k) mx = fmaxf(fmaxf(mx, elem(2 * k)), elem(2 * k + 1));
-    }
     // pairs m = 8 kb + 4 c + q hold keys 8 c + 2 q, +1 of key block kb
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -556,7 +565,6 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
         pf[BUF][kb][c] = __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
       }
     float psum = (part[0] + part[1]) + (part[2] + part[3]);
-    mx = max_with_partner(mx) * sl2;
     // The rare path below overwrites the speculative weights; without these
     // uses the compiler would sink their computation past the branch, out of
     // the interleaved slots.
@@ -565,7 +573,7 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
 #pragma unroll
       for (int c = 0; c < 2; ++c) asm volatile("" ::"v"(__builtin_bit_cast(i32x4, pf[BUF][kb][c])));
     asm volatile("" ::"v"(psum));
-    settle(std::integral_constant<int, (SK + 3) % 4>{}, sacc[BUF], t, mx, psum, pf[BUF]);
+    settle(std::integral_constant<int, (SK + 3) % 4>{}, sacc[BUF], t, psum, pf[BUF]);
     // operands of the next iteration's first P-V products: V of tile t, in
     // stage (SV + 1) % 4, published at the end of the previous iteration
     // (for t = 0, by the barrier before the loop)
