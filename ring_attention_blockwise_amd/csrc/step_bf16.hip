@@ -81,16 +81,28 @@ constexpr float kWeightCap = 256.0f;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Copies of one tensor (K or V) of one head into the LDS rings. Set up once
-// per work item: the head's base address in SGPRs and this lane's byte
-// offsets for the wave's kCopies 1 KB blocks of a tile (dma16_blocks).
+// per work item: this lane's byte offsets for the wave's kCopies 1 KB blocks
+// of a tile (dma16_blocks), and a cursor over the item's tiles in the order
+// they are requested, so that a copy costs a few scalar instructions: the
+// address of the next tile's first row and the bytes of the block from there
+// to its end (kv_len rows), restarted at the second key range.
 template <int D, bool IS_V>
 struct TileCopier {
   using Ly = Layout<D>;
-  uint64_t base;
   int voff[kCopies<D>];
+  uint64_t addr, addr1;  // next tile; start of the second range
+  int32_t left, left1;   // bytes from there to the end of the block
+  int32_t next, n0, ntiles;
 
-  __device__ __forceinline__ void init(const char* g, int wave, int lane) {
-    base = uniform_address(g);
+  __device__ __forceinline__ void init(const char* g, int wave, int lane, const TilePlan& plan, int64_t kv_len) {
+    const uint64_t base = uniform_address(g);
+    addr = base + (uint64_t)plan.r0.begin * Ly::kRowBytes;
+    left = ((int32_t)kv_len - plan.r0.begin) * Ly::kRowBytes;  // blocks are far below 2 GB
+    addr1 = base + (uint64_t)plan.r1.begin * Ly::kRowBytes;
+    left1 = ((int32_t)kv_len - plan.r1.begin) * Ly::kRowBytes;
+    next = 0;
+    n0 = plan.r0.ntiles;
+    ntiles = plan.total_tiles();
 #pragma unroll
     for (int i = 0; i < kCopies<D>; ++i) {
       // lane fills stored unit q of row r and fetches logical unit q ^ swz(r)
@@ -102,17 +114,25 @@ struct TileCopier {
     }
   }
 
-  // This wave's blocks of the tile of 64 rows starting at local row `start`
-  // into the LDS stage at `stage`. The buffer resource bounds the reads to
-  // the rows the block has: rows past kv_len read as zero. A tile past the
-  // last one (`exists` false) reads an empty range and fills its stage with
-  // zeros, which keeps the number of copies per iteration fixed (the stage it
-  // lands in is not read again).
-  __device__ __forceinline__ void copy(int64_t kv_len, int32_t start, bool exists, uint32_t stage, int wave) const {
-    const int32_t left = exists ? (int32_t)kv_len - start : 0;  // row counts are < 2^31
-    const int nbytes = (left < kBN ? left : kBN) * Ly::kRowBytes;
-    const uint64_t off = exists ? (uint64_t)start * Ly::kRowBytes : 0;
-    dma16_blocks<kCopies<D>>(resource_at(base, off, nbytes), stage + (uint32_t)(wave * kCopies<D> * 1024), voff);
+  // This wave's blocks of the next tile (64 rows) into the LDS stage at
+  // `stage`. The buffer resource bounds the reads to the rows the block has:
+  // rows past kv_len read as zero. A tile past the last one reads an empty
+  // range and fills its stage with zeros, which keeps the number of copies
+  // per iteration fixed (the stage it lands in is not read again).
+  __device__ __forceinline__ void copy_next(uint32_t stage, int wave) {
+    if (next == n0) {
+      addr = addr1;
+      left = left1;
+    }
+    const int32_t nb = next < ntiles ? (left < Ly::kTileBytes ? left : Ly::kTileBytes) : 0;
+    dma16_blocks<kCopies<D>>(resource_at(addr, 0, nb), stage + (uint32_t)(wave * kCopies<D> * 1024), voff);
+    addr += Ly::kTileBytes;
+    left -= Ly::kTileBytes;
+    ++next;
+  }
+  // Zeros into the LDS stage at `stage` (an empty range).
+  __device__ __forceinline__ void zero(uint32_t stage, int wave) const {
+    dma16_blocks<kCopies<D>>(resource_at(addr, 0, 0), stage + (uint32_t)(wave * kCopies<D> * 1024), voff);
   }
 };
 
@@ -256,14 +276,14 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
   const uint32_t smem_base = lds_address(smem);
   TileCopier<D, false> kcopy;
   TileCopier<D, true> vcopy;
-  kcopy.init(kg, wave, lane);
-  vcopy.init(vg, wave, lane);
+  kcopy.init(kg, wave, lane, plan, a.kv_len);
+  vcopy.init(vg, wave, lane, plan, a.kv_len);
+  // tiles are requested in order: K of t and V of t go to stage t % 4
   auto issue_k = [&](int t) {
-    kcopy.copy(a.kv_len, tile_start(t), t < ntiles, smem_base + (uint32_t)(t % kStages) * Ly::kTileBytes, wave);
+    kcopy.copy_next(smem_base + (uint32_t)(t % kStages) * Ly::kTileBytes, wave);
   };
   auto issue_v = [&](int t) {
-    vcopy.copy(a.kv_len, tile_start(t), t < ntiles, smem_base + Ly::kVBase + (uint32_t)(t % kStages) * Ly::kTileBytes,
-               wave);
+    vcopy.copy_next(smem_base + Ly::kVBase + (uint32_t)(t % kStages) * Ly::kTileBytes, wave);
   };
   // Piece j into staging slot `slot` (buffer-to-LDS), and the piece held in
   // staging out to the receive slot as piece j. Outside the share both use
@@ -290,7 +310,7 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
   issue_k(0);
   issue_k(1);
   issue_v(0);
-  vcopy.copy(a.kv_len, 0, false, smem_base + Ly::kVBase + 3u * Ly::kTileBytes, wave);
+  vcopy.zero(smem_base + Ly::kVBase + 3u * Ly::kTileBytes, wave);
 
   // ---- Q^T fragments (B operand of S^T = K Q^T) ------------------------------
   bf16x8 qf[Ly::kDChunks];
@@ -360,10 +380,13 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
   // Tile t's softmax: mask (partial tiles only), then the speculative
   // exponentials against the current reference. Returns the row maximum
   // (in base-2 units, this lane's pair combined) and the lane's sum.
+  // tiles of range r from index p_r on cross some row's causal boundary
+  const int32_t part0 = (plan.r0.full - plan.r0.begin) / kBN;
+  const int32_t part1 = plan.r0.ntiles + (plan.r1.full - plan.r1.begin) / kBN;
   auto mask_tile = [&](f32x16 (&s)[2], int t) {
     const bool first_range = t < plan.r0.ntiles;
-    const int32_t start = tile_start(t);
-    if (start + kBN > (first_range ? plan.r0.full : plan.r1.full)) {
+    if (t >= (first_range ? part0 : part1)) {
+      const int32_t start = tile_start(t);
       // keys [0, lim) are visible; this lane holds keys 4*hh + (a constant)
       const int32_t lim = (first_range ? vend0 : vend1) - start - 4 * hh;
 #pragma unroll
