@@ -224,7 +224,8 @@ def receive_modes(share, ws, out, lse, K, copy_stream, timed_ms, timed_mode, rou
     """The forward with each receive copy, and the same step kernels with no
     receive at all (ring_attn_step over the blocks in place, no finalize:
     the fused finalize of the last step writes less than a plain step, so
-    this baseline is, if anything, slightly slow). The modes are timed in
+    this baseline is, if anything, slightly slow). The forwards run without
+    a key split, as the baseline's steps do. The modes are timed in
     turn, `rounds` times over, and each reports its median (ms per forward),
     so that clock drift over the run does not favour one of them; overhead
     = forward / no-receive - 1."""
@@ -245,8 +246,10 @@ def receive_modes(share, ws, out, lse, K, copy_stream, timed_ms, timed_mode, rou
 
     state = harness.new_state(share)
 
+    # without a key split, like the step calls of the baseline
     def fwd(mode, cs):
-        return lambda: harness.run_forward(share, copy_stream=cs, workspace=ws, out=out, lse=lse, receive=mode)
+        return lambda: harness.run_forward(share, copy_stream=cs, workspace=ws, out=out, lse=lse, receive=mode,
+                                           key_split=1)
 
     modes = {"no_receive": lambda: harness.run_steps(share, range(wl.world), state=state),
              "fused": fwd("fused", None), "memcpy_side_stream": fwd("memcpy", copy_stream),
@@ -454,6 +457,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--receive", default="auto", choices=["auto", "memcpy", "fused"],
                     help="receive copy of the timed forwards (memcpy: hipMemcpyAsync on a side stream)")
+    ap.add_argument("--key-split", type=int, default=0,
+                    help="key split of the bf16 forward: 0 automatic (small shares), 1 never, 2..16 forced")
     ap.add_argument("--forwards-only", action="store_true",
                     help="time the forwards and skip every other measurement (for kernel traces)")
     ap.add_argument("--backward", action="store_true",
@@ -496,7 +501,9 @@ def main():
     launched = [s for s in range(wl.world) if pairs[s] > 0]
 
     out, lse = harness.alloc_outputs(share)
-    ws = harness.alloc_workspace(share)
+    ksplit = args.key_split
+    args.key_split_effective = harness.effective_key_split(share, ksplit)
+    ws = harness.alloc_workspace(share, key_split=ksplit)
     copy_stream = torch.cuda.Stream()
     cur = torch.cuda.current_stream()
     K, Wm = args.steps, args.warmup
@@ -504,7 +511,8 @@ def main():
 
     recv = args.receive
     for _ in range(Wm):
-        harness.run_forward(share, copy_stream=copy_stream, workspace=ws, out=out, lse=lse, receive=recv)
+        harness.run_forward(share, copy_stream=copy_stream, workspace=ws, out=out, lse=lse, receive=recv,
+                            key_split=ksplit)
     torch.cuda.synchronize()
     log(f"warmup done ({Wm} forwards)")
 
@@ -514,7 +522,7 @@ def main():
     wall0 = time.perf_counter()
     for i in range(K):
         harness.run_forward(share, copy_stream=copy_stream, workspace=ws, out=out, lse=lse,
-                            step_events=events[i], receive=recv)
+                            step_events=events[i], receive=recv, key_split=ksplit)
     stop.record(cur)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -543,7 +551,8 @@ def main():
         graph_ms = receive = hbm = probe = balance = cpu = None
         args.no_cpu_baseline = True
     else:
-        graph_ms, receive, hbm, probe, balance = extras(share, ws, out, lse, K, copy_stream, ms_per_step, recv, wl)
+        graph_ms, receive, hbm, probe, balance = extras(share, ws, out, lse, K, copy_stream, ms_per_step, recv, wl,
+                                                        ksplit)
     cpu = None
     if not args.no_cpu_baseline:
         if wl.local_len * wl.heads_q * wl.batch * wl.total_len <= SMALL_SHARE_PAIRS:
@@ -559,7 +568,7 @@ def main():
         ev.close()
 
 
-def extras(share, ws, out, lse, K, copy_stream, ms_per_step, recv, wl):
+def extras(share, ws, out, lse, K, copy_stream, ms_per_step, recv, wl, ksplit):
     """Graph replay, receive modes, HBM-bound kernels, matrix-core probe, load balance."""
     import torch
     from ring_attention_blockwise_amd import harness
@@ -568,7 +577,8 @@ def extras(share, ws, out, lse, K, copy_stream, ms_per_step, recv, wl):
     # work (every step kernel and receive copy), without per-launch host cost.
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        harness.run_forward(share, copy_stream=copy_stream, workspace=ws, out=out, lse=lse, receive=recv)
+        harness.run_forward(share, copy_stream=copy_stream, workspace=ws, out=out, lse=lse, receive=recv,
+                            key_split=ksplit)
     torch.cuda.synchronize()
     graph.replay()
     torch.cuda.synchronize()
@@ -615,6 +625,7 @@ def record(args, wl, rank, K, Wm, value, ms_per_step, bf16, total_flops, launche
             "global_seq_len": wl.total_len, "world": wl.world, "rank": rank, "partition": wl.partition,
             "ring_steps": wl.world, "parallelism": "one device's share of a simulated ring",
             "receive": args.receive,
+            "key_split": args.key_split_effective,
         },
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "effective_tflop_per_forward": round(total_flops / 1e12, 4),

@@ -148,7 +148,25 @@ typedef struct {
                                      1: block (rank + s) mod n ([HC]'s 6.1 text) */
   int32_t receive;                /* RA_RECV_*: how a block is copied into its
                                      receive slot (the result is the same) */
+  int32_t key_split;              /* bf16 forward: ways to split each query
+                                     tile's keys (0 = automatic, 1 = never,
+                                     2..16 = that many; see below) */
 } ra_ring_desc;
+
+/* Key split of the bf16 forward (desc->key_split). A step kernel runs one
+ * work item per 256-row query tile and head, one per compute unit at a time,
+ * so a small share leaves most of the 256 compute units idle while each item
+ * walks all of its key tiles. With a split of k every item runs as k parts,
+ * part j over its j-th share of the item's 64-key tiles, each from the empty
+ * state into a partial state of the workspace; a fold kernel after the step
+ * merges the incoming state and the k partials in order with one common
+ * reference (the block-combination rule of [HC] 6.2 applied k times) and
+ * writes the state, or the output on the last step. Automatic: shares with at
+ * most 128 work items get the largest power of two up to 8 that keeps items x
+ * k <= 256 and at least two key tiles per part; larger shares are not split.
+ * A given k is capped at the block's key tiles. The result is the same
+ * attention up to rounding (not bit for bit the unsplit one: the partial
+ * states are summed in a different order). fp32 forwards never split. */
 
 /* Receive copy of the ring drivers (desc->receive).
  * RA_RECV_MEMCPY: hipMemcpyAsync of the K and V block on copy_stream (or on
@@ -168,7 +186,9 @@ typedef struct {
 #define RA_RECV_FUSED  2
 
 /* Bytes of workspace ring_attn_forward needs: two receive slots for one K/V
- * block each, the fp32 state and alignment padding. Returns 0 on a bad desc. */
+ * block each, the fp32 state, the partial states of a key split (k fp32
+ * states; none without a split) and alignment padding. Returns 0 on a bad
+ * desc. */
 size_t ring_attn_forward_workspace_size(const ra_ring_desc* desc);
 
 /* Run the whole ring for one device: n steps, then finalize.

@@ -59,7 +59,7 @@ class RingDesc(ctypes.Structure):
         ("head_dim", ctypes.c_int32), ("local_len", ctypes.c_int64), ("dtype", ctypes.c_int32),
         ("causal", ctypes.c_int32), ("scale", ctypes.c_float), ("world", ctypes.c_int32),
         ("rank", ctypes.c_int32), ("partition", ctypes.c_int32), ("reverse_order", ctypes.c_int32),
-        ("receive", ctypes.c_int32),
+        ("receive", ctypes.c_int32), ("key_split", ctypes.c_int32),
     ]
 
 
@@ -153,11 +153,13 @@ def step_desc(batch, heads_q, heads_kv, head_dim, q_len, kv_len, dtype=BF16, cau
 
 
 def ring_desc(batch, heads_q, heads_kv, head_dim, local_len, world, rank, partition="zigzag",
-              dtype=BF16, causal=True, scale=0.0, reverse_order=False, receive="auto") -> RingDesc:
+              dtype=BF16, causal=True, scale=0.0, reverse_order=False, receive="auto",
+              key_split=0) -> RingDesc:
+    """key_split: 0 automatic, 1 never, 2..16 that many parts per query tile (bf16)."""
     part = PARTITIONS[partition] if isinstance(partition, str) else int(partition)
     recv = RECEIVES[receive] if isinstance(receive, str) else int(receive)
     return RingDesc(batch, heads_q, heads_kv, head_dim, local_len, dtype, int(causal), scale, world,
-                    rank, part, int(reverse_order), recv)
+                    rank, part, int(reverse_order), recv, int(key_split))
 
 
 def partition_segments(partition, world: int, rank: int, local_len: int):

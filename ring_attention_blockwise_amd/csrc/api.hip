@@ -165,17 +165,45 @@ hipError_t launch_step(const ra::StepArgs& a, int head_dim, int dtype, hipStream
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Compute units of an MI355X; a step launches one workgroup per compute unit
+// at a time (its LDS use), so a step with fewer work items than this leaves
+// compute units idle.
+constexpr int64_t kComputeUnits = 256;
+constexpr int32_t kMaxKeySplit = 16;
+
+// Ways the forward splits each query tile's keys (bf16 only): desc->key_split
+// when given (capped so that every part gets a key tile), else, for shares
+// with at most half as many 256-row work items as compute units, the largest
+// power of two up to 8 that keeps items x split within the compute units and
+// at least two 64-key tiles per part.
+int32_t key_split_of(const ra_ring_desc* d) {
+  if (d->dtype != RA_BF16 || d->key_split == 1) return 1;
+  const int64_t kv_tiles = (d->local_len + 63) / 64;
+  int64_t s = d->key_split;
+  if (s == 0) {
+    const int64_t items = (d->local_len + 255) / 256 * d->heads_q * (int64_t)d->batch;
+    s = 1;
+    while (s < 8 && items * s * 2 <= kComputeUnits && kv_tiles >= 4 * s) s *= 2;
+  }
+  if (s > kv_tiles) s = kv_tiles;
+  return s > 1 ? (int32_t)s : 1;
+}
+
 struct RingLayout {
   size_t block_bytes;  // one K (or V) block
   size_t state_rows;
+  int32_t split;       // key split of every step (1: none)
   size_t off_slot[2][2];
-  size_t off_o, off_m, off_l, total;
+  size_t off_o, off_m, off_l;
+  size_t off_po, off_pm, off_pl;  // partial states of a split step
+  size_t total;
 };
 
 bool ring_layout(const ra_ring_desc* d, RingLayout* L) {
   const size_t es = d->dtype == RA_BF16 ? 2 : 4;
   L->block_bytes = (size_t)d->batch * d->heads_kv * (size_t)d->local_len * d->head_dim * es;
   L->state_rows = (size_t)d->batch * d->heads_q * (size_t)d->local_len;
+  L->split = key_split_of(d);
   size_t off = 0;
   for (int s = 0; s < 2; ++s)
     for (int t = 0; t < 2; ++t) {
@@ -188,6 +216,13 @@ bool ring_layout(const ra_ring_desc* d, RingLayout* L) {
   off += align256(L->state_rows * 4);
   L->off_l = off;
   off += align256(L->state_rows * 4);
+  const size_t parts = L->split > 1 ? (size_t)L->split : 0;
+  L->off_po = off;
+  off += align256(parts * L->state_rows * d->head_dim * 4);
+  L->off_pm = off;
+  off += align256(parts * L->state_rows * 4);
+  L->off_pl = off;
+  off += align256(parts * L->state_rows * 4);
   L->total = off + 256;  // room to align the caller's base pointer
   return true;
 }
@@ -205,6 +240,8 @@ int check_ring_desc(const ra_ring_desc* d) {
   if (d->causal != 0 && d->causal != 1) return fail(RA_ERR_INVALID_ARG, "causal must be 0 or 1");
   if (d->receive < RA_RECV_AUTO || d->receive > RA_RECV_FUSED)
     return fail(RA_ERR_INVALID_ARG, "unknown receive %d", d->receive);
+  if (d->key_split < 0 || d->key_split > kMaxKeySplit)
+    return fail(RA_ERR_INVALID_ARG, "key_split %d out of range (0..%d)", d->key_split, kMaxKeySplit);
   ra_step_desc s{};
   s.batch = d->batch;
   s.heads_q = d->heads_q;
@@ -241,7 +278,7 @@ extern "C" {
 
 const char* ring_attn_last_error(void) { return g_last_error; }
 
-int32_t ring_attn_abi_version(void) { return 103; }
+int32_t ring_attn_abi_version(void) { return 104; }
 
 int ring_attn_partition_segments(int32_t partition, int32_t world, int32_t rank, int64_t local_len,
                                  ra_segment* segs, int32_t* n_segs) {
@@ -522,6 +559,12 @@ int forward_run(const ra_ring_desc* d, const RingLayout& L, const void* q_local,
         a.rx_dst[0] = slot_k[slot];
         a.rx_dst[1] = slot_v[slot];
         a.rx_bytes = (int64_t)L.block_bytes;
+      }
+      if (L.split > 1) {
+        a.split = L.split;
+        a.po = reinterpret_cast<float*>(base + L.off_po);
+        a.pm = reinterpret_cast<float*>(base + L.off_pm);
+        a.pl = reinterpret_cast<float*>(base + L.off_pl);
       }
       if ((e = launch_step(a, d->head_dim, d->dtype, cs)) != hipSuccess) return hip_fail(e, "step launch");
     }

@@ -52,6 +52,16 @@ struct StepArgs {
   int64_t rx_bytes;
   int64_t rx_share;
   int32_t rx_tile_lo;
+  // Key split (bf16 step only): split > 1 runs every query tile as `split`
+  // work items, item j over its share of the tile's key tiles, each starting
+  // from the empty state and writing a partial state j ([split][rows][D] in
+  // po, [split][rows] in pm and pl; rows = batch * heads_q * q_len). A fold
+  // launched after the step merges the incoming state (unless init) with the
+  // partials in order and writes the state, or the output when final_.
+  int32_t split;
+  float* po;
+  float* pm;
+  float* pl;
 };
 
 // The lazy-rescale threshold in base-2 exponent units: the reference m is
@@ -68,6 +78,8 @@ hipError_t launch_finalize(const float* o, const float* m, const float* l, void*
                            int64_t rows, int head_dim, int dtype, hipStream_t s);
 hipError_t launch_init_state(float* o, float* m, float* l, int64_t rows, int head_dim,
                              hipStream_t s);
+// The fold after a split step (see StepArgs::split).
+hipError_t launch_fold(const StepArgs& a, int64_t rows, int head_dim, int dtype, hipStream_t s);
 
 
 // ---- device helpers shared by the finalize kernel and the fused finalize of
@@ -204,6 +216,26 @@ __host__ __device__ __forceinline__ TilePlan plan_tiles(const StepArgs& a, int64
   p.r0 = has_x ? x : y;
   p.r1 = y;
   return p;
+}
+
+// The tiles [t0, t1) of a plan (in its order), as a plan of their own.
+template <int BN>
+__host__ __device__ __forceinline__ TilePlan restrict_plan(const TilePlan& p, int32_t t0, int32_t t1) {
+  const int32_t n0 = p.n > 0 ? p.r0.ntiles : 0;
+  const int32_t a0 = t0 < n0 ? t0 : n0, b0 = t1 < n0 ? t1 : n0;
+  const int32_t a1 = (t0 > n0 ? t0 : n0) - n0, b1 = (t1 > n0 ? t1 : n0) - n0;
+  KeyRange x = p.r0;
+  x.begin += a0 * BN;
+  x.ntiles = b0 - a0;
+  KeyRange y = p.r1;
+  y.begin += a1 * BN;
+  y.ntiles = p.n > 1 ? b1 - a1 : 0;
+  const bool has_x = x.ntiles > 0, has_y = y.ntiles > 0;
+  TilePlan q;
+  q.n = (has_x ? 1 : 0) + (has_y ? 1 : 0);
+  q.r0 = has_x ? x : y;
+  q.r1 = y;
+  return q;
 }
 
 // Exclusive end (local key index) of the keys of range r visible to a query

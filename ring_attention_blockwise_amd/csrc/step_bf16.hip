@@ -177,13 +177,17 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
   // others, so the heavy-first order is dealt round-robin over all XCDs.
   // Items whose tile is at or after rx_tile_lo carry a share of the fused
   // receive; rx_rank is their dense rank (-1: no share).
+  // With a key split, workgroup w runs part w % split of item w / split.
+  const int32_t split = a.split > 1 ? a.split : 1;
+  const int32_t vb = (int32_t)blockIdx.x / split;
+  const int32_t part = (int32_t)blockIdx.x % split;
   int32_t tile, b, h;
   int64_t rx_rank = -1;
   {
     const int32_t n_bk = a.batch * a.heads_kv;
     const int32_t rx_tiles = q_tiles - a.rx_tile_lo;
     if (n_bk % 8 == 0) {
-      const int32_t item = (int32_t)(blockIdx.x % 8) * items_per_xcd + (int32_t)(blockIdx.x / 8);
+      const int32_t item = (vb % 8) * items_per_xcd + vb / 8;
       if (item >= n_items) return;
       const int32_t per_kv = q_tiles * a.group;
       const int32_t bk = item / per_kv;
@@ -193,7 +197,7 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
       h = (bk % a.heads_kv) * a.group + rem % a.group;
       if (a.rx_bytes > 0 && rem < rx_tiles * a.group) rx_rank = (int64_t)bk * rx_tiles * a.group + rem;
     } else {
-      const int32_t item = (int32_t)blockIdx.x;
+      const int32_t item = vb;
       if (item >= n_items) return;
       const int32_t n_bh = a.batch * a.heads_q;
       tile = q_tiles - 1 - item / n_bh;
@@ -201,6 +205,7 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
       h = (item % n_bh) % a.heads_q;
       if (a.rx_bytes > 0 && item < rx_tiles * n_bh) rx_rank = item;
     }
+    if (rx_rank >= 0) rx_rank = rx_rank * split + part;
   }
   const int32_t kvh = h / a.group;
 
@@ -253,9 +258,19 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
   const int64_t r1 = (row0 + kBM < a.q_len) ? row0 + kBM : a.q_len;
   int64_t qmin, qmax;
   seg_range(a.qs, a.n_q_seg, row0, r1, &qmin, &qmax);
-  const TilePlan plan = plan_tiles<kBN>(a, qmin, qmax);
+  // A part of a split tile takes its share of the tile's key tiles, starts
+  // from the empty state and writes partial state `part`; the fold after the
+  // launch merges and finalizes.
+  const TilePlan plan = [&] {
+    const TilePlan p = plan_tiles<kBN>(a, qmin, qmax);
+    if (split == 1) return p;
+    const int32_t n = p.total_tiles();
+    return restrict_plan<kBN>(p, part * n / split, (part + 1) * n / split);
+  }();
   const int ntiles = plan.total_tiles();
-  if (ntiles == 0 && !a.init && !a.final_) {  // nothing visible, state untouched
+  const bool init = a.init || split > 1;
+  const bool fin = a.final_ && split == 1;
+  if (ntiles == 0 && !init && !fin) {  // nothing visible, state untouched
     rx_direct(0);
     return;
   }
@@ -265,6 +280,19 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
   const int64_t rowc = valid ? row : a.q_len - 1;
   const int64_t bh = (int64_t)b * a.heads_q + h;
   const size_t srow = (size_t)(bh * a.q_len + rowc);
+  // where the state goes: the running state, or partial `part`
+  const size_t prow = split > 1 ? (size_t)part * ((size_t)a.batch * a.heads_q * a.q_len) + srow : srow;
+  float* const o_dst = split > 1 ? a.po : a.o;
+  float* const m_dst = split > 1 ? a.pm : a.m;
+  float* const l_dst = split > 1 ? a.pl : a.l;
+  if (split > 1 && ntiles == 0) {  // an empty partial: the fold reads only its m
+    if (valid && hh == 0) {
+      m_dst[prow] = -INFINITY;
+      l_dst[prow] = 0.0f;
+    }
+    rx_direct(0);
+    return;
+  }
   const int64_t kv_off = ((int64_t)b * a.heads_kv + kvh) * a.kv_len * D;
   const char* kg = reinterpret_cast<const char*>(static_cast<const unsigned short*>(a.k) + kv_off);
   const char* vg = reinterpret_cast<const char*>(static_cast<const unsigned short*>(a.v) + kv_off);
@@ -323,7 +351,7 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
   // ---- running state: lane holds O^T rows d = 32*db + 8*(j/4) + 4*hh + j%4 ---
   f32x16 oacc[Ly::kDBlocks];
   float m_run, l_run;
-  if (a.init) {
+  if (init) {
 #pragma unroll
     for (int db = 0; db < Ly::kDBlocks; ++db)
 #pragma unroll
@@ -657,7 +685,7 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
   // ---- write back ---------------------------------------------------------------
   const float l_tot = sum_with_partner(l_run);
   if (!valid) return;
-  if (a.final_) {
+  if (fin) {
     const float inv = finalize_inv(l_tot);
     unsigned short* dst = static_cast<unsigned short*>(a.out) + srow * D;
 #pragma unroll
@@ -676,7 +704,7 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
       }
     if (hh == 0 && a.lse != nullptr) a.lse[srow] = finalize_lse(m_run, l_tot);
   } else {
-    float* op = a.o + srow * D;
+    float* op = o_dst + prow * D;
 #pragma unroll
     for (int db = 0; db < Ly::kDBlocks; ++db)
 #pragma unroll
@@ -684,8 +712,8 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
         *reinterpret_cast<float4*>(op + 32 * db + 8 * jj + 4 * hh) =
             make_float4(oacc[db][4 * jj], oacc[db][4 * jj + 1], oacc[db][4 * jj + 2], oacc[db][4 * jj + 3]);
     if (hh == 0) {
-      a.m[srow] = m_run;
-      a.l[srow] = l_tot;
+      m_dst[prow] = m_run;
+      l_dst[prow] = l_tot;
     }
   }
 }
@@ -696,9 +724,17 @@ hipError_t launch_step_bf16(const StepArgs& args, int head_dim, hipStream_t s) {
   const int64_t q_tiles = (args.q_len + kBM - 1) / kBM;
   const int64_t items = q_tiles * args.heads_q * args.batch;
   const int64_t per_xcd = (items + 7) / 8;
-  const dim3 grid((unsigned)(per_xcd * 8));
+  const int64_t split = args.split > 1 ? args.split : 1;
+  const dim3 grid((unsigned)(per_xcd * 8 * split));
   StepArgs a = args;
-  if (a.rx_bytes > 0) {
+  a.split = (int32_t)split;
+  if (a.rx_bytes > 0 && split > 1) {
+    // every part of every item carries an equal share
+    const int64_t carriers = items * split;
+    const int64_t per = (a.rx_bytes + carriers - 1) / carriers;
+    a.rx_tile_lo = 0;
+    a.rx_share = (per + kRxPiece - 1) / kRxPiece * kRxPiece;
+  } else if (a.rx_bytes > 0) {
     // Carriers of the receive: the items of query tiles lo .. q_tiles-1,
     // each taking rx_share bytes of both tensors, i.e. n = 2 * rx_share / 8 KB
     // pieces, moved in n + 2 receive iterations at most one in four
@@ -730,7 +766,9 @@ hipError_t launch_step_bf16(const StepArgs& args, int head_dim, hipStream_t s) {
     step_bf16_kernel<128><<<grid, kThreads, 0, s>>>(a, (int32_t)items, (int32_t)per_xcd, (int32_t)q_tiles);
   else
     step_bf16_kernel<64><<<grid, kThreads, 0, s>>>(a, (int32_t)items, (int32_t)per_xcd, (int32_t)q_tiles);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || split == 1) return e;
+  return launch_fold(a, (int64_t)a.batch * a.heads_q * a.q_len, head_dim, RA_BF16, s);
 }
 
 }  // namespace ra

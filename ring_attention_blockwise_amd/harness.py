@@ -37,10 +37,11 @@ def torch_dtype(wl):
     return torch.bfloat16 if wl.dtype == "bf16" else torch.float32
 
 
-def make_ring_desc(wl: ring_inputs.Workload, rank: int, reverse_order: bool = False, receive="auto") -> RingDesc:
+def make_ring_desc(wl: ring_inputs.Workload, rank: int, reverse_order: bool = False, receive="auto",
+                   key_split=0) -> RingDesc:
     return ring_desc(wl.batch, wl.heads_q, wl.heads_kv, wl.head_dim, wl.local_len, wl.world, rank,
                      wl.partition, dtype=dtype_code(wl), causal=wl.causal, reverse_order=reverse_order,
-                     receive=receive)
+                     receive=receive, key_split=key_split)
 
 
 @dataclasses.dataclass
@@ -52,8 +53,8 @@ class DeviceShare:
     v_blocks: list
     q_positions: np.ndarray     # global position of each local row
 
-    def ring_desc(self, reverse_order=False, receive="auto") -> RingDesc:
-        return make_ring_desc(self.workload, self.rank, reverse_order, receive)
+    def ring_desc(self, reverse_order=False, receive="auto", key_split=0) -> RingDesc:
+        return make_ring_desc(self.workload, self.rank, reverse_order, receive, key_split)
 
 
 def _to_device(x: np.ndarray, dt, device):
@@ -126,22 +127,33 @@ def alloc_outputs(share: DeviceShare):
     return out, lse
 
 
-def alloc_workspace(share: DeviceShare, reverse_order=False):
+def effective_key_split(share: DeviceShare, key_split=0) -> int:
+    """The key split the library gives this share's forward (1: none), read
+    from the workspace it asks for: k partial fp32 states of the share's rows."""
+    wl = share.workload
+    extra = (forward_workspace_size(share.ring_desc(key_split=key_split))
+             - forward_workspace_size(share.ring_desc(key_split=1)))
+    per = wl.batch * wl.heads_q * wl.local_len * (wl.head_dim + 2) * 4
+    return max(1, round(extra / per)) if extra > 0 else 1
+
+
+def alloc_workspace(share: DeviceShare, reverse_order=False, key_split=0):
     import torch
-    n = forward_workspace_size(share.ring_desc(reverse_order))
+    n = forward_workspace_size(share.ring_desc(reverse_order, key_split=key_split))
     return torch.empty(n, dtype=torch.uint8, device=share.q.device)
 
 
 def run_forward(share: DeviceShare, reverse_order=False, copy_stream=None, workspace=None, out=None, lse=None,
-                step_events=None, receive="auto"):
+                step_events=None, receive="auto", key_split=0):
     """ring_attn_forward on the current stream (receive copies on ``copy_stream``,
-    made as ``receive`` says: "auto", "memcpy" or "fused")."""
+    made as ``receive`` says: "auto", "memcpy" or "fused"; ``key_split`` as
+    ring_desc)."""
     if out is None:
         out, lse = alloc_outputs(share)
     if workspace is None:
-        workspace = alloc_workspace(share, reverse_order)
-    forward(share.ring_desc(reverse_order, receive), share.q, share.k_blocks, share.v_blocks, out, lse, workspace,
-            copy_stream=copy_stream, step_events=step_events)
+        workspace = alloc_workspace(share, reverse_order, key_split)
+    forward(share.ring_desc(reverse_order, receive, key_split), share.q, share.k_blocks, share.v_blocks, out, lse,
+            workspace, copy_stream=copy_stream, step_events=step_events)
     return out, lse
 
 

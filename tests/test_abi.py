@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert ra.lib().ring_attn_abi_version() == 103
+    assert ra.lib().ring_attn_abi_version() == 104
 
 
 def _expand(segs):
@@ -171,6 +171,44 @@ def test_forward_rejects_small_workspace_and_bad_desc():
     same = ctypes.c_void_p(0x5000)
     assert L.ring_attn_forward(ctypes.byref(rd), FAKE, blocks, blocks, FAKE, FAKE, FAKE, ws, same, same,
                                None) == ra.ERR_INVALID_ARG
+
+
+def test_key_split_workspace_and_validation():
+    """The key split's partial states are sized into the forward workspace:
+    k fp32 states (O, m, l) for a split of k; automatic only for small bf16
+    shares; a given k is capped at the block's key tiles; out-of-range values
+    are rejected before anything is enqueued."""
+    L = ra.lib()
+    blocks = (ctypes.c_void_p * 8)(*([0x10000] * 8))
+    ws = ctypes.c_size_t(1 << 40)
+
+    def size(**kw):
+        return ra.forward_workspace_size(ra.ring_desc(1, 8, 8, 128, 1024, 8, 0, **kw))
+
+    rows = 8 * 1024
+    def parts(k):
+        return k * rows * 128 * 4 + 2 * k * rows * 4   # every region is a multiple of 256 bytes here
+
+    base = size(key_split=1)
+    assert size() == base + parts(8)                       # 32 work items: split 8 ways (2 key tiles each)
+    assert size(key_split=2) == base + parts(2)
+    assert size(key_split=16) == base + parts(16)          # 16 key tiles: one each
+    # a 256-row block has 4 key tiles: 16 is capped at 4
+    assert (ra.forward_workspace_size(ra.ring_desc(1, 8, 8, 128, 256, 8, 0, key_split=16))
+            - ra.forward_workspace_size(ra.ring_desc(1, 8, 8, 128, 256, 8, 0, key_split=1))) == 4 * 2048 * 520
+    # fp32 never splits; 128K/8 GQA (2048 work items) is not split automatically
+    assert ra.forward_workspace_size(ra.ring_desc(1, 8, 8, 128, 1024, 8, 0, dtype=ra.F32, key_split=8)) == \
+        ra.forward_workspace_size(ra.ring_desc(1, 8, 8, 128, 1024, 8, 0, dtype=ra.F32))
+    big = dict(batch=1, heads_q=32, heads_kv=8, head_dim=128, local_len=16384, world=8, rank=0)
+    assert ra.forward_workspace_size(ra.ring_desc(**big)) == ra.forward_workspace_size(ra.ring_desc(**big, key_split=1))
+    for k in (-1, 17):
+        bad = ra.ring_desc(1, 8, 8, 128, 1024, 8, 0, key_split=k)
+        assert L.ring_attn_forward_workspace_size(ctypes.byref(bad)) == 0
+        assert L.ring_attn_forward(ctypes.byref(bad), FAKE, blocks, blocks, FAKE, FAKE, FAKE, ws, None, None,
+                                   None) == ra.ERR_INVALID_ARG
+        assert "key_split" in ra.last_error()
+    # the split share still fits the no-allocation forward's scratch
+    assert size() - 256 <= ra.NOALLOC_SCRATCH_BYTES
 
 
 def test_ulysses_workspace_and_validation():

@@ -69,17 +69,53 @@ def test_small_workload_all_rows(gpu, name):
 
 @pytest.mark.parametrize("name", ["ring4_noncausal_f32", "zigzag8k_8dev_d128"])
 def test_forward_equals_manual_loop_bitwise(gpu, name):
+    """Without a key split (which the 8K/8 share would get by default) the
+    driver's steps are exactly ring_attn_step + ring_attn_finalize."""
     import torch
     wl = W[name]
     share = harness.build_share(wl, 0, gpu)
-    out_f, lse_f = harness.run_forward(share, copy_stream=_copy_stream())  # default receive
-    out_c, lse_c = harness.run_forward(share, copy_stream=_copy_stream(), receive="memcpy")
-    out_s, lse_s = harness.run_forward(share, copy_stream=None, receive="memcpy")  # on the compute stream
+    out_f, lse_f = harness.run_forward(share, copy_stream=_copy_stream(), key_split=1)  # default receive
+    out_c, lse_c = harness.run_forward(share, copy_stream=_copy_stream(), receive="memcpy", key_split=1)
+    out_s, lse_s = harness.run_forward(share, copy_stream=None, receive="memcpy", key_split=1)  # compute stream
     st = harness.run_steps(share, range(wl.world))
     out_m, lse_m = harness.finalize_state(share, st)
     torch.cuda.synchronize()
     for o, s in ((out_f, lse_f), (out_c, lse_c), (out_s, lse_s)):
         assert torch.equal(o, out_m) and torch.equal(s, lse_m)
+
+
+# Key split: forced and automatic splits of small shares, with ragged key
+# tiles (520 rows: 9 tiles, the last of 8 keys; a split of 16 is capped at
+# 9), head_dim 64, GQA groups and a non-causal ring; every row of the device
+# against the oracle, and the same bits on a second run.
+_SPLIT_CASES = [
+    ("zigzag8k_8dev_d128", 0, {}, 2),
+    ("zigzag8k_8dev_d128", 7, {}, 16),
+    ("zigzag8k_8dev_d128", 1, dict(heads_q=6, heads_kv=3, world=4, local_len=520), 0),
+    ("zigzag8k_8dev_d128", 2, dict(heads_q=6, heads_kv=3, world=4, local_len=520), 16),
+    ("zigzag8k_8dev_d128", 5, dict(head_dim=64), 8),
+    ("zigzag8k_8dev_d128", 4, dict(heads_q=8, heads_kv=2), 4),
+    ("zigzag8k_8dev_d128", 1, dict(world=4, local_len=512, causal=False), 8),
+]
+
+
+@pytest.mark.parametrize("name,rank,kw,split", _SPLIT_CASES)
+def test_key_split_matches_oracle(gpu, name, rank, kw, split):
+    import torch
+    wl = W[name].with_(**kw) if kw else W[name]
+    print(f"{name} rank {rank} {kw} key_split={split}", flush=True)
+    rows = np.arange(wl.local_len)
+    share, ref_o, ref_l = _oracle_for(wl, rank, rows)
+    ws = harness.alloc_workspace(share, key_split=split)
+    ws.fill_(255)  # partial states never read before they are written
+    out, lse = harness.run_forward(share, copy_stream=_copy_stream(), workspace=ws, key_split=split)
+    torch.cuda.synchronize()
+    first = (out.clone(), lse.clone())
+    _check(out, lse, rows, ref_o, ref_l, wl.dtype)
+    ws.fill_(255)
+    out, lse = harness.run_forward(share, copy_stream=None, workspace=ws, key_split=split, receive="memcpy")
+    torch.cuda.synchronize()
+    assert torch.equal(out, first[0]) and torch.equal(lse, first[1])
 
 
 # Shares for the fused receive: the full-size ones the benchmark times, a
