@@ -658,6 +658,20 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
 
   if (ntiles > 0) {
     scores(I0{}, sacc[0]);  // S of tile 0 (stage 0)
+    // A row without a reference yet (an empty incoming state) takes tile 0's
+    // maximum as its reference here, as the rare path of iteration 0 would
+    // (same value), so iteration 0's speculative weights are final and its
+    // rare path runs only for rows that see no key of tile 0.
+    if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0) {
+      mask_tile(sacc[0], 0);
+      float mx = sacc[0][0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[0][kb][j]);
+      mx = max_with_partner(mx) * sl2;
+      if (m_run == -INFINITY) m_run = mx;
+    }
 #pragma unroll
     for (int k = 0; k < kPre; ++k) vpre[k] = read_vt<D, 3>(k, v_addr);  // "tile -1": zeros
     // iteration t: K of t+1 in stage (t+1)%4, V of t-1 in (t-1)%4, buffer t%2
