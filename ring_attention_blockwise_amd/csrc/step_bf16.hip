@@ -161,7 +161,9 @@ constexpr int kind_index(int k) {
   return n;
 }
 
-template <int D>
+// SPLIT: the launch of a key-split step (parts and partial states); the
+// unsplit instantiation carries none of that code.
+template <int D, bool SPLIT>
 __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t n_items, int32_t items_per_xcd,
                                                              int32_t q_tiles) {
   using Ly = Layout<D>;
@@ -178,7 +180,7 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
   // Items whose tile is at or after rx_tile_lo carry a share of the fused
   // receive; rx_rank is their dense rank (-1: no share).
   // With a key split, workgroup w runs part w % split of item w / split.
-  const int32_t split = a.split > 1 ? a.split : 1;
+  const int32_t split = SPLIT ? a.split : 1;
   const int32_t vb = (int32_t)blockIdx.x / split;
   const int32_t part = (int32_t)blockIdx.x % split;
   int32_t tile, b, h;
@@ -285,7 +287,7 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
   float* const o_dst = split > 1 ? a.po : a.o;
   float* const m_dst = split > 1 ? a.pm : a.m;
   float* const l_dst = split > 1 ? a.pl : a.l;
-  if (split > 1 && ntiles == 0) {  // an empty partial: the fold reads only its m
+  if (SPLIT && ntiles == 0) {  // an empty partial: the fold reads only its m
     if (valid && hh == 0) {
       m_dst[prow] = -INFINITY;
       l_dst[prow] = 0.0f;
@@ -776,10 +778,18 @@ hipError_t launch_step_bf16(const StepArgs& args, int head_dim, hipStream_t s) {
     a.rx_tile_lo = (int32_t)best;
     a.rx_share = share_of(best);
   }
-  if (head_dim == 128)
-    step_bf16_kernel<128><<<grid, kThreads, 0, s>>>(a, (int32_t)items, (int32_t)per_xcd, (int32_t)q_tiles);
-  else
-    step_bf16_kernel<64><<<grid, kThreads, 0, s>>>(a, (int32_t)items, (int32_t)per_xcd, (int32_t)q_tiles);
+  const int32_t ni = (int32_t)items, px = (int32_t)per_xcd, qt = (int32_t)q_tiles;
+  if (head_dim == 128) {
+    if (split > 1)
+      step_bf16_kernel<128, true><<<grid, kThreads, 0, s>>>(a, ni, px, qt);
+    else
+      step_bf16_kernel<128, false><<<grid, kThreads, 0, s>>>(a, ni, px, qt);
+  } else {
+    if (split > 1)
+      step_bf16_kernel<64, true><<<grid, kThreads, 0, s>>>(a, ni, px, qt);
+    else
+      step_bf16_kernel<64, false><<<grid, kThreads, 0, s>>>(a, ni, px, qt);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || split == 1) return e;
   return launch_fold(a, (int64_t)a.batch * a.heads_q * a.q_len, head_dim, RA_BF16, s);
