@@ -86,8 +86,10 @@ def test_forward_equals_manual_loop_bitwise(gpu, name):
 
 # Key split: forced and automatic splits of small shares, with ragged key
 # tiles (520 rows: 9 tiles, the last of 8 keys; a split of 16 is capped at
-# 9), head_dim 64, GQA groups and a non-causal ring; every row of the device
-# against the oracle, and the same bits on a second run.
+# 9), head_dim 64, GQA groups, a non-causal ring, batch 2, the striped and
+# contiguous partitions and a split of 3 (not a power of two) over 10 key
+# tiles; every row of the device against the oracle, and the same bits on a
+# second run.
 _SPLIT_CASES = [
     ("zigzag8k_8dev_d128", 0, {}, 2),
     ("zigzag8k_8dev_d128", 7, {}, 16),
@@ -96,6 +98,9 @@ _SPLIT_CASES = [
     ("zigzag8k_8dev_d128", 5, dict(head_dim=64), 8),
     ("zigzag8k_8dev_d128", 4, dict(heads_q=8, heads_kv=2), 4),
     ("zigzag8k_8dev_d128", 1, dict(world=4, local_len=512, causal=False), 8),
+    ("zigzag8k_8dev_d128", 3, dict(batch=2, heads_q=4, heads_kv=2, world=4, local_len=384), 0),
+    ("zigzag8k_8dev_d128", 2, dict(partition="striped", world=4, local_len=512), 4),
+    ("zigzag8k_8dev_d128", 0, dict(partition="contiguous", world=4, local_len=640, head_dim=64), 3),
 ]
 
 
