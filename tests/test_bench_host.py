@@ -45,3 +45,42 @@ def test_cpu_baseline_reports_host_and_extrapolation():
     assert rec["os_cpu_count"] == os.cpu_count() and rec["cores"] >= 1
     assert "cpu_model" in rec and rec["blas_threads"] is not None
     assert rec["full_share_s_extrapolated"] == pytest.approx(1.0 / rec["value"], rel=1e-2)
+
+
+def test_bench_line_keeps_the_contract():
+    """The JSON line the benchmark prints: the contract's keys and types, the
+    workload named in config (no model keys), the roofline and the CPU
+    baseline objects (built here from fixed numbers, no GPU)."""
+    import argparse
+    import json
+    import numpy as np
+    wl = ring_inputs.WORKLOADS["zigzag128k_8dev_gqa"]
+    args = argparse.Namespace(receive="auto", key_split_effective=1)
+    roof_traffic = 763735326
+    cpu = {"value": 0.05, "unit": "TFLOP/s", "cores": 16, "kind": "oracle", "sample": "rows x heads"}
+    rec = bench.record(args, wl, 0, 20, 3, 1250.0, 14.07, True, 17.59e12, list(range(8)), 1.73, np.full(8, 1.73),
+                       1272.75, bench.PEAK_BF16_TFLOPS, roof_traffic, None, None, None, None, bench.load_balance(wl),
+                       cpu)
+    line = json.loads(json.dumps(rec))
+    for key, typ in (("metric", str), ("value", float), ("unit", str), ("n_gpus", int), ("steps", int),
+                     ("warmup", int), ("ms_per_step", float), ("higher_is_better", bool), ("scaling", str),
+                     ("dtype", str), ("data", str), ("config", dict)):
+        assert isinstance(line[key], typ), key
+    assert line["n_gpus"] == 1 and line["steps"] == 20 and line["warmup"] == 3
+    assert line["higher_is_better"] is True and line["scaling"] == "weak" and line["vs_baseline"] is None
+    assert line["dtype"] == "bf16" and line["unit"] == "TFLOP/s"
+    assert line["config"]["workload"] == "zigzag128k_8dev_gqa" and "model" not in line["config"]
+    roof = line["roofline"]
+    assert roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s" and roof["peak"] == 2500.0
+    assert roof["frac"] == pytest.approx(1272.75 / 2500.0, abs=1e-4) and roof["traffic"] == roof_traffic
+    assert line["cpu_baseline"]["kind"] == "oracle" and line["cpu_baseline"]["cores"] == 16
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import json
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "one GPU" in msg["error"]
