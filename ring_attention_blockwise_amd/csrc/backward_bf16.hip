@@ -41,6 +41,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #ifndef RA_BWD_SCHED
 #define RA_BWD_SCHED 0
 #endif
+#ifndef RA_DQ_AHEAD
+#define RA_DQ_AHEAD 3
+#endif
 #ifndef RA_BWD_AHEAD
 #define RA_BWD_AHEAD 8
 #endif
@@ -301,16 +304,24 @@ __global__ void __launch_bounds__(kQWaves * 64) bwd_dq_kernel(BwdArgs a, int32_t
     // live, which keeps the wave within its registers. On the last iteration
     // (v == ntiles) the S and dP products read a stage holding an older tile
     // and are never used.
-    if (v > 0) {
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc)
-#pragma unroll
-        for (int db = 0; db < kDB; ++db) {
-          const bf16x8 kt = read_tr(lo, hi, db, sp + kc * 16 * kRowB);
-          dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsf[kc >> 1][kc & 1], dqa[db], 0, 0, 0);
-        }
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    // One stream of products with their LDS operands read AH products
+    // ahead, fenced per product: dQ of tile v-1 (if any), then S and dP of
+    // tile v.
+    constexpr int AH = RA_DQ_AHEAD;
+    constexpr int NQ = 4 * kDB;   // dQ products
+    constexpr int NS = 4 * kDC;   // S and dP products
+    const int first = v > 0 ? 0 : NQ;
+    constexpr int NT = NQ + NS;
+    bf16x8 op[NT];
+    auto rd = [&](int i) {
+      if (i < NQ) {
+        op[i] = read_tr(lo, hi, i % kDB, sp + (i / kDB) * 16 * kRowB);
+      } else {
+        const int j = i - NQ;  // j = 4 c + 2 kb + (0: K, 1: V)
+        const int c = j >> 2, kb = (j >> 1) & 1, isv = j & 1;
+        op[i] = *lds_ptr<bf16x8>(k_addr[c] + so + (isv ? kTileB : 0) + kb * 32 * kRowB);
+      }
+    };
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -319,14 +330,25 @@ __global__ void __launch_bounds__(kQWaves * 64) bwd_dq_kernel(BwdArgs a, int32_t
         pacc[kb][j] = 0.0f;
       }
 #pragma unroll
-    for (int c = 0; c < kDC; ++c)
+    for (int i = 0; i < AH; ++i)
+      if (first + i < NT) rd(first + i);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kf = *lds_ptr<bf16x8>(k_addr[c] + so + kb * 32 * kRowB);
-        const bf16x8 vf = *lds_ptr<bf16x8>(k_addr[c] + so + kTileB + kb * 32 * kRowB);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sacc[kb], 0, 0, 0);
-        pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, of[c], pacc[kb], 0, 0, 0);
+    for (int i = 0; i < NT; ++i) {
+      if (i < first) continue;
+      if (i + AH < NT) rd(i + AH);
+      if (i < NQ) {
+        const int kc = i / kDB, db = i % kDB;
+        dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], dsf[kc >> 1][kc & 1], dqa[db], 0, 0, 0);
+      } else {
+        const int j = i - NQ;
+        const int c = j >> 2, kb = (j >> 1) & 1, isv = j & 1;
+        if (isv)
+          pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], of[c], pacc[kb], 0, 0, 0);
+        else
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], qf[c], sacc[kb], 0, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (v < ntiles) {
       next_phase();
       // ---- V_v: P and dS of tile v, packed as the B operand of dQ
