@@ -41,6 +41,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #ifndef RA_BWD_SCHED
 #define RA_BWD_SCHED 0
 #endif
+#ifndef RA_KV_AHEAD
+#define RA_KV_AHEAD 3
+#endif
 #ifndef RA_DQ_AHEAD
 #define RA_DQ_AHEAD 3
 #endif
@@ -604,15 +607,28 @@ bwd_dkdv_kernel(BwdArgs a, int32_t k_tiles) {
           pacc[rb][4 * jj + i] = e4[i];
         }
       }
+    {
+      // the products in one fenced stream, LDS operands read AH ahead
+      constexpr int AH = RA_KV_AHEAD;
+      constexpr int N = 4 * kDC;  // i = 4 c + 2 rb + (0: S, 1: dP)
+      bf16x8 op[N];
+      auto rd = [&](int i) {
+        const int c = i >> 2, rb = (i >> 1) & 1, isp = i & 1;
+        op[i] = *lds_ptr<bf16x8>(q_addr[c] + so + (isp ? kKOffDo : 0) + rb * 32 * kRowB);
+      };
 #pragma unroll
-    for (int c = 0; c < kDC; ++c)
+      for (int i = 0; i < AH; ++i) rd(i);
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const bf16x8 qa = *lds_ptr<bf16x8>(q_addr[c] + so + rb * 32 * kRowB);
-        const bf16x8 oa = *lds_ptr<bf16x8>(q_addr[c] + so + kKOffDo + rb * 32 * kRowB);
-        sacc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[c], sacc[rb], 0, 0, 0);
-        pacc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[c], pacc[rb], 0, 0, 0);
+      for (int i = 0; i < N; ++i) {
+        if (i + AH < N) rd(i + AH);
+        const int c = i >> 2, rb = (i >> 1) & 1;
+        if (i & 1)
+          pacc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], vf[c], pacc[rb], 0, 0, 0);
+        else
+          sacc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], kf[c], sacc[rb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    }
 #if RA_BWD_SCHED
     // the 16 row-term reads first (they start the accumulators), then the
     // operand reads RA_BWD_AHEAD MFMAs ahead of their use
