@@ -307,50 +307,79 @@ __global__ void __launch_bounds__(kQWaves * 64) bwd_dq_kernel(BwdArgs a, int32_t
     // live, which keeps the wave within its registers. On the last iteration
     // (v == ntiles) the S and dP products read a stage holding an older tile
     // and are never used.
-    // One stream of products with their LDS operands read AH products
-    // ahead, fenced per product: dQ of tile v-1 (if any), then S and dP of
-    // tile v.
-    constexpr int AH = RA_DQ_AHEAD;
-    constexpr int NQ = 4 * kDB;   // dQ products
-    constexpr int NS = 4 * kDC;   // S and dP products
-    const int first = v > 0 ? 0 : NQ;
-    constexpr int NT = NQ + NS;
-    bf16x8 op[NT];
-    auto rd = [&](int i) {
-      if (i < NQ) {
-        op[i] = read_tr(lo, hi, i % kDB, sp + (i / kDB) * 16 * kRowB);
-      } else {
-        const int j = i - NQ;  // j = 4 c + 2 kb + (0: K, 1: V)
-        const int c = j >> 2, kb = (j >> 1) & 1, isv = j & 1;
-        op[i] = *lds_ptr<bf16x8>(k_addr[c] + so + (isv ? kTileB : 0) + kb * 32 * kRowB);
+    if constexpr (D == 128) {
+      // One stream of products with their LDS operands read AH products
+      // ahead, fenced per product: dQ of tile v-1 (if any), then S and dP of
+      // tile v.
+      constexpr int AH = RA_DQ_AHEAD;
+      constexpr int NQ = 4 * kDB;   // dQ products
+      constexpr int NS = 4 * kDC;   // S and dP products
+      const int first = v > 0 ? 0 : NQ;
+      constexpr int NT = NQ + NS;
+      bf16x8 op[NT];
+      auto rd = [&](int i) {
+        if (i < NQ) {
+          op[i] = read_tr(lo, hi, i % kDB, sp + (i / kDB) * 16 * kRowB);
+        } else {
+          const int j = i - NQ;  // j = 4 c + 2 kb + (0: K, 1: V)
+          const int c = j >> 2, kb = (j >> 1) & 1, isv = j & 1;
+          op[i] = *lds_ptr<bf16x8>(k_addr[c] + so + (isv ? kTileB : 0) + kb * 32 * kRowB);
+        }
+      };
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          sacc[kb][j] = 0.0f;
+          pacc[kb][j] = 0.0f;
+        }
+#pragma unroll
+      for (int i = 0; i < AH; ++i)
+        if (first + i < NT) rd(first + i);
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        if (i < first) continue;
+        if (i + AH < NT) rd(i + AH);
+        if (i < NQ) {
+          const int kc = i / kDB, db = i % kDB;
+          dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], dsf[kc >> 1][kc & 1], dqa[db], 0, 0, 0);
+        } else {
+          const int j = i - NQ;
+          const int c = j >> 2, kb = (j >> 1) & 1, isv = j & 1;
+          if (isv)
+            pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], of[c], pacc[kb], 0, 0, 0);
+          else
+            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], qf[c], sacc[kb], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-    };
+    } else {  // at head_dim 64 the compiler's own schedule is faster
+      if (v > 0) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+        for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        sacc[kb][j] = 0.0f;
-        pacc[kb][j] = 0.0f;
-      }
-#pragma unroll
-    for (int i = 0; i < AH; ++i)
-      if (first + i < NT) rd(first + i);
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      if (i < first) continue;
-      if (i + AH < NT) rd(i + AH);
-      if (i < NQ) {
-        const int kc = i / kDB, db = i % kDB;
-        dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], dsf[kc >> 1][kc & 1], dqa[db], 0, 0, 0);
-      } else {
-        const int j = i - NQ;
-        const int c = j >> 2, kb = (j >> 1) & 1, isv = j & 1;
-        if (isv)
-          pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], of[c], pacc[kb], 0, 0, 0);
-        else
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], qf[c], sacc[kb], 0, 0, 0);
+          for (int db = 0; db < kDB; ++db) {
+            const bf16x8 kt = read_tr(lo, hi, db, sp + kc * 16 * kRowB);
+            dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsf[kc >> 1][kc & 1], dqa[db], 0, 0, 0);
+          }
       }
       __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          sacc[kb][j] = 0.0f;
+          pacc[kb][j] = 0.0f;
+        }
+#pragma unroll
+      for (int c = 0; c < kDC; ++c)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 kf = *lds_ptr<bf16x8>(k_addr[c] + so + kb * 32 * kRowB);
+          const bf16x8 vf = *lds_ptr<bf16x8>(k_addr[c] + so + kTileB + kb * 32 * kRowB);
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sacc[kb], 0, 0, 0);
+          pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, of[c], pacc[kb], 0, 0, 0);
+        }
     }
     if (v < ntiles) {
       next_phase();
@@ -607,27 +636,39 @@ bwd_dkdv_kernel(BwdArgs a, int32_t k_tiles) {
           pacc[rb][4 * jj + i] = e4[i];
         }
       }
-    {
-      // the products in one fenced stream, LDS operands read AH ahead
-      constexpr int AH = RA_KV_AHEAD;
-      constexpr int N = 4 * kDC;  // i = 4 c + 2 rb + (0: S, 1: dP)
-      bf16x8 op[N];
-      auto rd = [&](int i) {
-        const int c = i >> 2, rb = (i >> 1) & 1, isp = i & 1;
-        op[i] = *lds_ptr<bf16x8>(q_addr[c] + so + (isp ? kKOffDo : 0) + rb * 32 * kRowB);
-      };
+    if constexpr (D == 128) {
+      {
+        // the products in one fenced stream, LDS operands read AH ahead
+        constexpr int AH = RA_KV_AHEAD;
+        constexpr int N = 4 * kDC;  // i = 4 c + 2 rb + (0: S, 1: dP)
+        bf16x8 op[N];
+        auto rd = [&](int i) {
+          const int c = i >> 2, rb = (i >> 1) & 1, isp = i & 1;
+          op[i] = *lds_ptr<bf16x8>(q_addr[c] + so + (isp ? kKOffDo : 0) + rb * 32 * kRowB);
+        };
 #pragma unroll
-      for (int i = 0; i < AH; ++i) rd(i);
+        for (int i = 0; i < AH; ++i) rd(i);
 #pragma unroll
-      for (int i = 0; i < N; ++i) {
-        if (i + AH < N) rd(i + AH);
-        const int c = i >> 2, rb = (i >> 1) & 1;
-        if (i & 1)
-          pacc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], vf[c], pacc[rb], 0, 0, 0);
-        else
-          sacc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], kf[c], sacc[rb], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < N; ++i) {
+          if (i + AH < N) rd(i + AH);
+          const int c = i >> 2, rb = (i >> 1) & 1;
+          if (i & 1)
+            pacc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], vf[c], pacc[rb], 0, 0, 0);
+          else
+            sacc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], kf[c], sacc[rb], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
+    } else {  // at head_dim 64 the compiler's own schedule is faster
+#pragma unroll
+      for (int c = 0; c < kDC; ++c)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const bf16x8 qa = *lds_ptr<bf16x8>(q_addr[c] + so + rb * 32 * kRowB);
+          const bf16x8 oa = *lds_ptr<bf16x8>(q_addr[c] + so + kKOffDo + rb * 32 * kRowB);
+          sacc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[c], sacc[rb], 0, 0, 0);
+          pacc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[c], pacc[rb], 0, 0, 0);
+        }
     }
 #if RA_BWD_SCHED
     // the 16 row-term reads first (they start the accumulators), then the
