@@ -25,9 +25,12 @@
 //    than 8 in base-2 units (so every weight stays <= 2^8), rescales O and l,
 //    and recomputes the weights (identical ones where nothing was raised).
 //  * K and V tiles are copied HBM -> LDS by 16-byte buffer-to-LDS loads into
-//    two rings of four stages each: K of tile t+3 at the start of iteration
-//    t, V of tile t+2 in its middle (every wave copies one eighth of each),
-//    so a copy has one and a half to two iterations to land. One workgroup
+//    two rings of four stages each: K of tile t+3 after the first few
+//    products of iteration t (issued behind queued products rather than by
+//    all eight waves at once right after the barrier, where they queue at
+//    the compute unit's address unit), V of tile t+2 in its middle (every
+//    wave copies one eighth of each), so a copy has about one and a half
+//    iterations to land. One workgroup
 //    barrier per iteration, at the end of iteration t, publishes K of tile
 //    t+2 and V of tile t+1 (V of tile t+1 is first read at the end of
 //    iteration t+1, for the first P-V products of the next iteration). Each
@@ -59,6 +62,7 @@ constexpr int kBM = kWaves * 32;  // query rows per workgroup
 static_assert(kStages == 4, "the K/V rings below have four stages each");
 constexpr int kKAhead = 3;        // K of tile t + kKAhead is requested at the start of iteration t
 constexpr int kVAhead = 2;        // V of tile t + kVAhead is requested in the middle of iteration t
+constexpr int kKSlot = 6;         // the product slot of an iteration that requests K
 
 #ifndef RA_PIPE_AHEAD
 #define RA_PIPE_AHEAD 3
@@ -534,9 +538,7 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
     constexpr int BUF = decltype(buf_tag)::value;
     constexpr int NM = NP + NS;      // products per iteration
     constexpr int EPS = 32 / NM;     // softmax elements per slot
-    // K of tile t+3 goes to the stage of K of tile t-1 (last read before the
-    // previous barrier)
-    issue_k(t + kKAhead);
+    static_assert(kKSlot < NM / 2, "K is requested before V");
     // receive: fetch piece r, store piece r-2 (from the slot after r's)
     const bool rx_on = decltype(rx_tag)::value && t == rx_next && rx_r < n_rx + 2;
     const int32_t r = rx_r;
@@ -599,7 +601,10 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
 #pragma unroll
       for (int m = 0; m < 16; ++m)
         if ((2 * m + 1) / EPS + 2 == k) pairs[m] = __builtin_convertvector((f32x2){p[2 * m], p[2 * m + 1]}, bf16x2);
-      if (k == NM / 2) issue_v(t + kVAhead);  // V of tile t+2 (its stage held V of tile t-2)
+      // K of tile t+3 goes to the stage of K of tile t-1 (last read before
+      // the previous barrier), V of tile t+2 to that of V of tile t-2
+      if (k == kKSlot) issue_k(t + kKAhead);
+      if (k == NM / 2) issue_v(t + kVAhead);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
