@@ -45,7 +45,7 @@
  * State.     (O, m, l) is kept in base 2: with t_j = log2(e) * scale * q.k_j,
  *            O = sum_j 2^(t_j - m) v_j and l = sum_j 2^(t_j - m) over the keys
  *            folded so far. m is a reference exponent no smaller than
- *            max_j t_j - 8 (it is raised lazily, which is exact: any reference
+ *            max_j t_j - 32 (it is raised lazily, which is exact: any reference
  *            gives the same O / l). The empty state is m = -inf, l = 0, O = 0.
  *            This is [HC]'s (M, L, O) with M expressed in base 2.
  */

@@ -66,8 +66,11 @@ struct StepArgs {
 
 // The lazy-rescale threshold in base-2 exponent units: the reference m is
 // only raised when the running maximum exceeds it by more than this, so every
-// weight 2^(t - m) stays <= 2^8.
-constexpr float kRescaleThreshold = 8.0f;
+// weight 2^(t - m) stays <= 2^32. Sums of such weights over any block stay far
+// inside fp32 range (2^32 per weight, below 2^63 for 2^31 keys), and bf16 P
+// carries fp32's exponent range, so a higher threshold costs no precision; it
+// only makes the rescales rarer on rows whose maximum keeps climbing.
+constexpr float kRescaleThreshold = 32.0f;
 
 // Launchers (each returns hipGetLastError() of its launch).
 hipError_t launch_step_bf16(const StepArgs& a, int head_dim, hipStream_t s);

@@ -18,11 +18,11 @@
 //    by side in both of its waves.
 //  * The exponentials of tile t are taken against the current reference
 //    maximum, and the tile's maximum is not computed on the main path: a
-//    weight can exceed 2^8 only if the lane's sum of the tile's weights does,
+//    weight can exceed 2^32 only if the lane's sum of the tile's weights does,
 //    so that sum (needed for l anyway) decides. Only then, or on a row's
 //    first visible tile, the rare path recomputes the tile's scores, takes
 //    their maximum, raises the reference where the maximum passes it by more
-//    than 8 in base-2 units (so every weight stays <= 2^8), rescales O and l,
+//    than 32 in base-2 units (so every weight stays <= 2^32), rescales O and l,
 //    and recomputes the weights (identical ones where nothing was raised).
 //  * K and V tiles are copied HBM -> LDS by 16-byte buffer-to-LDS loads into
 //    two rings of four stages each: K of tile t+3 after the first few
@@ -81,7 +81,8 @@ constexpr int kRxStageBytes = kRxSlots * kRxPiece;
 
 // A lane's speculative weights of one tile sum past this only if one of them
 // may exceed 2^kRescaleThreshold (each is >= 0).
-constexpr float kWeightCap = 256.0f;
+constexpr float kWeightCap = 4294967296.0f;  // 2^32
+static_assert(kRescaleThreshold == 32.0f, "kWeightCap is 2^kRescaleThreshold");
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Copies of one tensor (K or V) of one head into the LDS rings. Set up once
@@ -470,8 +471,8 @@ __global__ void __launch_bounds__(kThreads) step_bf16_kernel(StepArgs a, int32_t
   // scores and weights. O must already hold the products of tile t-1 (the
   // compiler orders the rescale after them).
   auto settle = [&](auto st_tag, f32x16 (&s)[2], int t, float& psum, bf16x8 (&pb)[2][2]) {
-    // Every speculative weight is <= 2^8 unless this lane's sum of them
-    // passed 2^8 (or overflowed): only then, or while the row has no
+    // Every speculative weight is <= 2^32 unless this lane's sum of them
+    // passed 2^32 (or overflowed): only then, or while the row has no
     // reference yet (its first visible tile), is the tile's maximum needed.
     if (__builtin_amdgcn_ballot_w64(!(psum <= kWeightCap) || m_run == -INFINITY) != 0) {
       scores(st_tag, s);
